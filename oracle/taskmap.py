@@ -1,0 +1,144 @@
+"""Integer reference of the Assign work split — oracle side, test infrastructure.
+
+Parity status: pinned by invariants (tests/test_oracle_taskmap.py: every
+active unit is owned by exactly one worker, no worker exceeds L units, the
+split counts match a direct per-worker walk, slots never exceed twice the
+number of workers, and unit counts match a brute-force count of visible
+keys per tile).  The pages fix only the idea, not the constants, so the
+constants below are this library's own specification; the HIP Assign kernel
+must reproduce this map bit for bit.
+
+Pages followed:
+* "Triton-TLE rewrite of Tencent HPC-Ops Attention", §1.2: Assign cuts every
+  KV sequence into tiles and builds a load-balanced task map from the work per
+  CTA; §3.3: choose the chunk length from the total load first, then cut each
+  request by its real KV length, and let a task owned by one CTA write its
+  result directly.
+* "vLLM Triton Attention Backend Deep Dive", §3: Q blocks pack all query heads
+  of one KV head (and several query tokens) into one work item; a persistent
+  grid of fixed size reads its work from metadata in GPU memory.
+
+Specification
+-------------
+* Q-blocks, in (sequence b, kv head g, first token t0) order.  With
+  G = Hq / Hkv and q_len = query tokens of b: if q_len * G <= 16 the single
+  Q-block (b, g, 0, q_len) holds every query token of (b, g) ("small",
+  decode-like); otherwise Q-blocks hold nt = 128 / G tokens:
+  (b, g, t0, min(nt, q_len - t0)) for t0 = 0, nt, 2 nt, ... ("large").
+  Row r of a Q-block is token t0 + r // G, query head g * G + r % G.
+* A unit is one 64-key tile of one Q-block that holds at least one key some
+  row of the Q-block may see (in the coarse sense below).  With
+  pos_lo = seq_len - q_len + t0 and pos_hi = pos_lo + nt - 1:
+  hi = min(seq_len - 1, pos_hi) if causal else seq_len - 1;
+  lo = window_left(pos_lo) if window > 0 else 0;  no units if hi < lo;
+  tiles tile_lo = lo // 64 .. tile_hi = hi // 64.  With a block mask, a tile
+  t counts only if mask[b, hm, qt, (64 t) // tile] is 1 for some query tile
+  qt in [pos_lo // tile, pos_hi // tile] and some head hm of the Q-block
+  (hm = 0 when the mask is shared across heads).
+* U = total units; the units of Q-block q are S_q .. S_q + n_q - 1 in the
+  order above (S = exclusive prefix sum of n).
+* L = force_split_units if it is > 0, else max(split_min_units, ceil(U / P)).
+  Worker w owns units [w L, min((w + 1) L, U)); there are ceil(U / L) workers.
+* n_splits(q) = 0 if n_q == 0, else floor((S_q + n_q - 1) / L) - floor(S_q / L) + 1.
+  Q-blocks with n_splits != 1 go, in order, into the combine list.
+  Q-blocks with n_splits >= 2 get partial slots slot_base(q) = running sum of
+  n_splits over earlier such Q-blocks (-1 for the others); n_slots = total.
+"""
+import numpy as np
+
+UNIT_KEYS = 64
+SMALL_MAX_ROWS = 16
+LARGE_ROWS = 128
+
+
+def _window_left(pos, window, expand, chunk):
+    left = max(0, pos - window + 1)
+    if expand and chunk > 0:
+        left = (left // chunk) * chunk
+    return left
+
+
+def q_blocks(seq_lens, query_start_loc, Hq, Hkv):
+    G = Hq // Hkv
+    out = []
+    for b in range(len(seq_lens)):
+        ql = int(query_start_loc[b + 1]) - int(query_start_loc[b])
+        if ql <= 0:
+            continue
+        if ql * G <= SMALL_MAX_ROWS:
+            for g in range(Hkv):
+                out.append((b, g, 0, ql))
+        else:
+            nt = LARGE_ROWS // G
+            for g in range(Hkv):
+                for t0 in range(0, ql, nt):
+                    out.append((b, g, t0, min(nt, ql - t0)))
+    return out
+
+
+def unit_count(desc, seq_lens, query_start_loc, Hq, Hkv, *, causal, window, expand_to_chunk,
+               landmark_chunk, block_mask=None, block_mask_tile=128):
+    b, g, t0, nt = desc
+    G = Hq // Hkv
+    ctx = int(seq_lens[b])
+    ql = int(query_start_loc[b + 1]) - int(query_start_loc[b])
+    pos_lo = ctx - ql + t0
+    pos_hi = pos_lo + nt - 1
+    hi = min(ctx - 1, pos_hi) if causal else ctx - 1
+    lo = _window_left(pos_lo, window, expand_to_chunk, landmark_chunk) if window > 0 else 0
+    if hi < lo:
+        return 0
+    t_lo, t_hi = lo // UNIT_KEYS, hi // UNIT_KEYS
+    if block_mask is None:
+        return t_hi - t_lo + 1
+    heads = [0] if block_mask.shape[1] == 1 else list(range(g * G, (g + 1) * G))
+    qts = range(pos_lo // block_mask_tile, pos_hi // block_mask_tile + 1)
+    n = 0
+    for t in range(t_lo, t_hi + 1):
+        kt = (t * UNIT_KEYS) // block_mask_tile
+        if any(block_mask[b, hm, qt, kt] for hm in heads for qt in qts):
+            n += 1
+    return n
+
+
+def build(seq_lens, query_start_loc, *, Hq, Hkv, num_workers, split_min_units=8,
+          force_split_units=0, causal=True, window=0, window_expand_to_chunk=True,
+          landmark_chunk=0, block_mask=None, block_mask_tile=128):
+    seq_lens = [int(x) for x in seq_lens]
+    qsl = [int(x) for x in query_start_loc]
+    descs = q_blocks(seq_lens, qsl, Hq, Hkv)
+    n = [unit_count(dsc, seq_lens, qsl, Hq, Hkv, causal=causal, window=window,
+                    expand_to_chunk=window_expand_to_chunk, landmark_chunk=landmark_chunk,
+                    block_mask=block_mask, block_mask_tile=block_mask_tile) for dsc in descs]
+    prefix = [0]
+    for x in n:
+        prefix.append(prefix[-1] + x)
+    U = prefix[-1]
+    P = int(num_workers)
+    if force_split_units > 0:
+        L = int(force_split_units)
+    else:
+        L = max(int(split_min_units), -(-U // P))
+    n_splits, slot_base, combine_list = [], [], []
+    slots = 0
+    for q, x in enumerate(n):
+        S = prefix[q]
+        ns = 0 if x == 0 else (S + x - 1) // L - S // L + 1
+        n_splits.append(ns)
+        if ns != 1:
+            combine_list.append(q)
+        if ns >= 2:
+            slot_base.append(slots)
+            slots += ns
+        else:
+            slot_base.append(-1)
+    return {
+        "desc": np.array(descs, dtype=np.int32).reshape(-1, 4),
+        "n_units": np.array(n, dtype=np.int32),
+        "unit_prefix": np.array(prefix, dtype=np.int32),
+        "n_splits": np.array(n_splits, dtype=np.int32),
+        "slot_base": np.array(slot_base, dtype=np.int32),
+        "combine_list": np.array(combine_list, dtype=np.int32),
+        "U": U, "P": P, "L": L, "n_qb": len(descs), "n_slots": slots,
+        "n_workers": -(-U // L) if U else 0,
+    }

@@ -1,0 +1,114 @@
+"""Pins for oracle.taskmap: invariants any correct work split must satisfy."""
+import numpy as np
+import pytest
+
+from attention_paged_kv_attn_amd import workloads as W
+from oracle import brute, taskmap
+
+
+def _check_invariants(tm):
+    U, L, P = tm["U"], tm["L"], tm["P"]
+    prefix, n = tm["unit_prefix"], tm["n_units"]
+    assert prefix[0] == 0 and prefix[-1] == U and np.all(np.diff(prefix) == n)
+    nw = tm["n_workers"]
+    assert nw == (-(-U // L) if U else 0)
+    owner_count = np.zeros(U, dtype=np.int64)
+    splits = np.zeros(tm["n_qb"], dtype=np.int64)
+    for w in range(nw):
+        a, b = w * L, min((w + 1) * L, U)
+        assert 0 < b - a <= L
+        owner_count[a:b] += 1
+        # Q-blocks this worker touches, by direct walk
+        for q in range(tm["n_qb"]):
+            if n[q] and prefix[q] < b and prefix[q + 1] > a:
+                splits[q] += 1
+    assert np.all(owner_count == 1)                          # every unit owned exactly once
+    assert np.array_equal(splits, tm["n_splits"])
+    assert np.array_equal(tm["combine_list"], np.nonzero(tm["n_splits"] != 1)[0])
+    sb = tm["slot_base"]
+    run = 0
+    for q in range(tm["n_qb"]):
+        if tm["n_splits"][q] >= 2:
+            assert sb[q] == run
+            run += tm["n_splits"][q]
+        else:
+            assert sb[q] == -1
+    assert run == tm["n_slots"] <= 2 * max(nw, 1)
+
+
+@pytest.mark.parametrize("P", [1, 7, 64, 512])
+def test_decode_split_invariants(P):
+    rng = np.random.default_rng(2)
+    ctx = W.decode_ctx_lengths(rng, 64, 128, 32768)
+    for ql in (1, 2, 4):
+        qsl = np.arange(65) * ql
+        tm = taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=P)
+        assert tm["n_qb"] == 64 * 8
+        _check_invariants(tm)
+        assert tm["U"] == 8 * int(sum((c - 1) // 64 + 1 for c in ctx))
+
+
+def test_hybrid_and_forced_split():
+    ctx = [8704] + list(range(1024, 1024 + 63 * 200, 200))
+    ql = [512] + [1] * 63
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    tm = taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=512)
+    assert tm["n_qb"] == 8 * (16 + 63)
+    _check_invariants(tm)
+    tm1 = taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=512, force_split_units=1)
+    assert tm1["L"] == 1 and tm1["n_slots"] == sum(x for x in tm1["n_units"] if x >= 2)
+    _check_invariants(tm1)
+
+
+def _brute_units(desc, ctx, ql, **rule):
+    """Count 64-key tiles holding a key visible to some row of the Q-block."""
+    b, g, t0, nt = desc
+    tiles = set()
+    for i in range(t0, t0 + nt):
+        pos = ctx - ql + i
+        for j in range(ctx):
+            if brute.is_visible(pos, j, ctx, **rule):
+                tiles.add(j // 64)
+    return len(tiles)
+
+
+@pytest.mark.parametrize("rule", [dict(causal=True), dict(causal=False),
+                                  dict(causal=True, window=200, chunk=64),
+                                  dict(causal=True, window=150, expand_to_chunk=False, chunk=32)])
+def test_unit_counts_match_brute_visibility(rule):
+    ctx = [37, 300, 700, 130]
+    ql = [1, 40, 200, 3]
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    kw = dict(causal=rule.get("causal", True), window=rule.get("window", 0),
+              window_expand_to_chunk=rule.get("expand_to_chunk", True),
+              landmark_chunk=rule.get("chunk", 0))
+    tm = taskmap.build(ctx, qsl, Hq=8, Hkv=2, num_workers=5, **kw)
+    for desc, n in zip(tm["desc"], tm["n_units"]):
+        b = desc[0]
+        exact = _brute_units(tuple(desc), ctx[b], ql[b], **rule)
+        if rule.get("expand_to_chunk", True) or not rule.get("chunk"):
+            assert n == exact
+        else:
+            # the unit range is set by the window and causal bounds alone: a tile at
+            # the window edge may hold nothing but a landmark key, so the count is
+            # the window-only count, never below the exact visible-tile count
+            coarse = _brute_units(tuple(desc), ctx[b], ql[b], **dict(rule, chunk=0))
+            assert n == coarse and exact <= n
+
+
+def test_block_mask_unit_counts():
+    rng = np.random.default_rng(4)
+    L_ = 1024
+    nq = L_ // 128
+    mask = (rng.random((2, 1, nq, nq)) > 0.7).astype(np.uint8)
+    mask[:, :, np.arange(nq), np.arange(nq)] = 1
+    ctx = [L_, L_]
+    qsl = [0, L_, 2 * L_]
+    tm = taskmap.build(ctx, qsl, Hq=8, Hkv=2, num_workers=16, block_mask=mask)
+    _check_invariants(tm)
+    for desc, n in zip(tm["desc"], tm["n_units"]):
+        b, g, t0, nt = desc
+        # Q-blocks of 32 tokens never straddle a 128-token query tile here, so the
+        # count is exact: tiles with a visible key under causal + mask
+        want = _brute_units(tuple(desc), L_, L_, causal=True, mask=mask[b, 0].tolist())
+        assert n == want
