@@ -5,14 +5,12 @@ kernels: Assign -> split-K attention -> combine); ``binding`` marshals torch
 tensors into its calls.  Importing this package loads nothing; the library is
 loaded on first use and its absence is an error, never a fallback.
 """
-__all__ = ["binding", "workloads"]
+import importlib
+
+__all__ = ["binding", "workloads", "build"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    if name == "workloads":
-        from . import workloads
-        return workloads
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

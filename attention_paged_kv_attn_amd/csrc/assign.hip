@@ -1,0 +1,174 @@
+// assign.hip — the Assign stage: one workgroup builds the task map.
+//
+// "Triton-TLE rewrite of Tencent HPC-Ops Attention", §1.2: Assign cuts every
+// KV sequence into tiles and produces a load-balanced, GPU-resident task map
+// for the persistent split-K workgroups; §3.3: the chunk length is chosen from
+// the total load first, then each request is cut by its own KV length.  The
+// map is integer-only and must equal the CPU specification bit for bit:
+//   Q-blocks in (b, g, t0) order; n_units = active 64-key tiles; prefix S;
+//   L = force ? force : max(L_min, ceil(U / P)); worker w owns [wL, (w+1)L);
+//   n_splits(q) = 0 | floor((S+n-1)/L) - floor(S/L) + 1; combine list = the
+//   Q-blocks with n_splits != 1; slot_base = running sum over split Q-blocks.
+#include "pa_device.h"
+
+namespace pa {
+
+constexpr int kAssignThreads = 1024;
+
+// Exclusive prefix sum over the workgroup; *total gets the sum.  `sh` holds
+// kAssignThreads / 64 + 1 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kAssignThreads / 64 ? sh[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(w, d);
+      if (lane >= d) w += y;
+    }
+    if (lane < kAssignThreads / 64) sh[lane] = w;      // inclusive wave totals
+    if (lane == kAssignThreads / 64 - 1) sh[kAssignThreads / 64] = w;
+  }
+  __syncthreads();
+  const int base = wave ? sh[wave - 1] : 0;
+  *total = sh[kAssignThreads / 64];
+  __syncthreads();
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
+  __shared__ int sh[kAssignThreads / 64 + 1];
+  __shared__ int err;
+  const int tid = threadIdx.x;
+  if (tid == 0) err = E_NONE;
+  __syncthreads();
+
+  // 0. metadata checks: qsl is a non-decreasing prefix ending at total_q, q_len <= seq_len
+  for (int b = tid; b < p.B; b += kAssignThreads) {
+    const int a = p.qsl[b], c = p.qsl[b + 1];
+    if ((b == 0 && a != 0) || c < a || (b == p.B - 1 && c != p.total_q)) atomicMax(&err, (int)E_QSL);
+    else if (c - a > p.seq_lens[b]) atomicMax(&err, (int)E_QLEN);
+  }
+  __syncthreads();
+  if (err != E_NONE) {
+    if (tid == 0) {
+      for (int i = 0; i < kHeaderInts; ++i) p.hdr[i] = 0;
+      p.hdr[H_P] = p.P;
+      p.hdr[H_ERROR] = err;
+      p.hdr[H_MAXSLOTS] = p.max_slots;
+    }
+    return;
+  }
+
+  // 1. Q-blocks per sequence -> first Q-block index of each sequence
+  const int nt_large = kLargeRows / p.G;
+  int carry = 0, tot;
+  for (int c0 = 0; c0 < p.B; c0 += kAssignThreads) {
+    const int b = c0 + tid;
+    int nqb = 0;
+    if (b < p.B) {
+      const int ql = p.qsl[b + 1] - p.qsl[b];
+      nqb = ql <= 0 ? 0 : (ql * p.G <= kSmallMaxRows ? 1 : (ql + nt_large - 1) / nt_large);
+      nqb *= p.Hkv;
+    }
+    const int ex = block_exclusive_scan(nqb, &tot, sh);
+    if (b < p.B) p.seq_qb_base[b] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) p.seq_qb_base[p.B] = carry;
+  const int n_qb = carry;
+  __syncthreads();
+
+  // 2. descriptors and unit counts (counts parked in unit_prefix[q + 1])
+  for (int q = tid; q < n_qb; q += kAssignThreads) {
+    int lo = 0, hi = p.B - 1;                      // last b with base[b] <= q
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq_qb_base[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int per_g = (p.seq_qb_base[b + 1] - p.seq_qb_base[b]) / p.Hkv;
+    const int rem = q - p.seq_qb_base[b];
+    const int g = rem / per_g, t = rem % per_g;
+    const int q0 = p.qsl[b], ql = p.qsl[b + 1] - q0, ctx = p.seq_lens[b];
+    const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
+    const int t0 = t * ntl;
+    const int nt = min(ntl, ql - t0);
+    reinterpret_cast<int4*>(p.qb_desc)[q] = make_int4(b, g, t0, nt);
+    const int pos_lo = ctx - ql + t0, pos_hi = pos_lo + nt - 1;
+    int t_lo, t_hi, n = 0;
+    if (qblock_tiles(p, ctx, pos_lo, pos_hi, t_lo, t_hi)) {
+      if (p.bm == nullptr) {
+        n = t_hi - t_lo + 1;
+      } else {
+        for (int tl = t_lo; tl <= t_hi; ++tl) n += mask_union(p, b, g, pos_lo, pos_hi, tl) ? 1 : 0;
+      }
+    }
+    p.unit_prefix[q + 1] = n;
+  }
+  __syncthreads();
+
+  // 3. unit prefix
+  carry = 0;
+  for (int c0 = 0; c0 < n_qb; c0 += kAssignThreads) {
+    const int q = c0 + tid;
+    const int n = q < n_qb ? p.unit_prefix[q + 1] : 0;
+    const int ex = block_exclusive_scan(n, &tot, sh);
+    if (q < n_qb) p.unit_prefix[q + 1] = carry + ex + n;
+    carry += tot;
+  }
+  if (tid == 0) p.unit_prefix[0] = 0;
+  const int U = carry;
+  const int L = p.force_L > 0 ? p.force_L : max(p.L_min, (U + p.P - 1) / p.P);
+  __syncthreads();
+
+  // 4. splits, combine list, partial slots
+  int c_carry = 0, s_carry = 0, ctot, stot;
+  for (int c0 = 0; c0 < n_qb; c0 += kAssignThreads) {
+    const int q = c0 + tid;
+    int ns = 1;
+    if (q < n_qb) {
+      const int S = p.unit_prefix[q], n = p.unit_prefix[q + 1] - S;
+      ns = n == 0 ? 0 : (S + n - 1) / L - S / L + 1;
+      p.n_splits[q] = ns;
+    }
+    const int in_c = (q < n_qb && ns != 1) ? 1 : 0;
+    const int in_s = (q < n_qb && ns >= 2) ? ns : 0;
+    const int cx = block_exclusive_scan(in_c, &ctot, sh);
+    const int sx = block_exclusive_scan(in_s, &stot, sh);
+    if (q < n_qb) {
+      if (in_c) p.combine_list[c_carry + cx] = q;
+      p.slot_base[q] = in_s ? s_carry + sx : -1;
+    }
+    c_carry += ctot;
+    s_carry += stot;
+  }
+  if (tid == 0) {
+    const bool over = s_carry > p.max_slots;
+    p.hdr[H_U] = over ? 0 : U;
+    p.hdr[H_P] = p.P;
+    p.hdr[H_L] = L;
+    p.hdr[H_NQB] = n_qb;
+    p.hdr[H_NSLOTS] = s_carry;
+    p.hdr[H_NCOMBINE] = over ? 0 : c_carry;
+    p.hdr[H_NWORKERS] = over ? 0 : (U ? (U + L - 1) / L : 0);
+    p.hdr[H_ERROR] = over ? E_SLOTS : E_NONE;
+    p.hdr[H_MAXSLOTS] = p.max_slots;
+    for (int i = H_MAXSLOTS + 1; i < kHeaderInts; ++i) p.hdr[i] = 0;
+  }
+}
+
+hipError_t launch_assign(const KParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,968 @@
+// attention.hip — the persistent split-K attention kernel (Split-K stage).
+//
+// "Triton-TLE rewrite of Tencent HPC-Ops Attention", §1.2: persistent
+// workgroups walk the task map; per KV tile they compute QK, the mask, an fp32
+// online softmax and PV, and emit either the final output (a Q-block owned by
+// one worker) or a partial output + LSE (split Q-blocks, merged by Combine).
+// The same kernel serves decode rows and prefill chunks in one launch
+// ("Chunked Prefill kernel optimisation: Triton hybrid attention": one fused
+// kernel for a hybrid batch) and reads its work from GPU metadata with a grid
+// of fixed size ("vLLM Triton Attention Backend Deep Dive", §3, persistent
+// kernels).
+//
+// gfx950 design (not the Hopper TMA / WGMMA / warp-specialised design of the
+// pages): every product runs on 16x16 MFMA in the transposed form
+//     S^T = K Q^T   (M = 16 keys, N = 16 query rows, K = head dims)
+//     O^T = V^T P^T (M = 16 dims, N = 16 query rows, K = keys)
+// so a lane always owns one query row: the 16x16 accumulator layout gives lane
+// l the column l % 16 and rows 4 (l / 16) + j.  The row max and row sum of the
+// online softmax are then in-lane plus two cross-lane steps, the rescale of
+// the O accumulator needs no shuffle, and the P operand of the PV product is
+// built from the lane's own S values (the key order inside a PV K-step is
+// chosen to match; V is gathered in that same order).  This is the small-M
+// idea of the Triton-TLE page (§3.1, KV tile on the MFMA M side, query heads
+// on N) carried through both products.
+//
+// Two Q-block shapes:
+//  * small (q_len * G <= 16 rows, decode / MTP): memory-bound.  The four
+//    waves of a workgroup take disjoint runs of the worker's units and load
+//    K and V straight from HBM into MFMA operand registers (K rows are already
+//    k-contiguous; V rows are transposed in registers with byte permutes).
+//    The four partial states are merged through LDS at the end.
+//  * large (128 rows = 128 / G tokens x G heads, prefill): compute-bound.
+//    Each wave owns 32 rows; K and V tiles are staged once per workgroup into
+//    LDS in MFMA-operand order and double-buffered.
+// Block-sparse prefill compacts the active tiles of a Q-block with a 64-lane
+// ballot + mbcnt prefix into an LDS list ("Triton-TLE ...", §2.1).
+#include <type_traits>
+
+#include "pa_device.h"
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int KIND, int D>
+struct Cfg {
+  static constexpr int MD = D / 16;                                  // O^T M-blocks; V elements per lane per row load
+  static constexpr int KSQ = KIND == KIND_F32 ? D / 4 : D / 32;      // QK K-steps
+  static constexpr int ELT = KIND == KIND_F32 ? 4 : KIND == KIND_BF16 ? 2 : 1;
+  static constexpr int K_TILE = 64 * D * ELT;                        // LDS bytes, K tile (operand order)
+  static constexpr int V_TILE = 64 * D * (KIND == KIND_F32 ? 4 : 2);  // V staged as bf16 for fp8
+  static constexpr int STAGE = K_TILE + V_TILE;
+  static constexpr int MERGE = kWaves * kSmallMaxRows * (D + 2) * 4;  // small-path wave merge
+  static constexpr int LDS = (2 * STAGE > MERGE ? 2 * STAGE : MERGE) + kMaskListCap * 2;
+};
+
+template <int KIND> struct QKOpT;
+template <> struct QKOpT<KIND_F32> { using T = float; };
+template <> struct QKOpT<KIND_BF16> { using T = bf16x8; };
+template <> struct QKOpT<KIND_F8> { using T = long; };
+
+__device__ __forceinline__ f32x4 mfma_qk(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_qk(long a, long b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_pv(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};          // round to nearest even
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// Two E4M3FN bytes (bits 0-7 and 8-15 of w) -> two bf16 in one word, exactly.
+// The byte's low 7 bits placed at float bits 20..26 form the float
+// 2^(e-127) * 1.m (e >= 1) or the denormal m * 2^-129 (e == 0); scaling by
+// 2^120 gives 2^(e-7) * 1.m or m * 2^-9, the E4M3 value.  Four significant
+// bits fit bf16 exactly, so the top half of the float is the bf16.
+// (NaN codes map to 480; they only occur in slots that are never visible and
+// are zeroed before use.)
+__device__ __forceinline__ unsigned f8x2_to_bf16x2(unsigned w) {
+  const float k = 0x1p120f;
+  const float f0 = __builtin_bit_cast(float, ((w & 0x7Fu) << 20) | ((w & 0x80u) << 24)) * k;
+  const float f1 = __builtin_bit_cast(float, ((w & 0x7F00u) << 12) | ((w & 0x8000u) << 16)) * k;
+  return (__builtin_bit_cast(unsigned, f0) >> 16) | (__builtin_bit_cast(unsigned, f1) & 0xFFFF0000u);
+}
+
+// ---------------------------------------------------------------------------
+// addressing.  Every load address is valid: keys past the end of a sequence
+// are clamped to its last key (their probability is exactly 0, so the finite
+// data they bring contributes nothing), and a block-table entry outside
+// [0, num_pages) is replaced by page 0 and reported in the error word.
+// ---------------------------------------------------------------------------
+struct SeqCtx {
+  int b, g, ctx, t_lo;
+  const int32_t* bt_row;
+};
+
+__device__ __forceinline__ int page_of(const KParams& p, const SeqCtx& s, int key) {
+  const int idx = key >> p.page_shift;
+  int page = idx < p.max_pages ? s.bt_row[idx] : -1;
+  if ((unsigned)page >= (unsigned)p.num_pages) {
+    p.hdr[H_ERROR] = E_PAGE;
+    page = 0;
+  }
+  return page;
+}
+
+// Rows of one 64-key tile.  FAST (page_size >= 64): the tile lies in one page,
+// so the page lookup and the row base are uniform (scalar) and each lane adds a
+// 32-bit offset.  Otherwise every key looks up its own page.
+template <int ELT, bool FAST>
+struct Tile {
+  const char* kb;
+  const char* vb;
+  int J0, nvalid;
+  uint32_t kss, vss;   // bytes between consecutive keys of a page
+
+  __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s, int tile) {
+    J0 = tile * kUnitKeys;
+    nvalid = min(kUnitKeys, s.ctx - J0);
+    kss = (uint32_t)(p.k_ss * ELT);
+    vss = (uint32_t)(p.v_ss * ELT);
+    if constexpr (FAST) {
+      const int page = page_of(p, s, J0);
+      const int slot = J0 & (p.page_size - 1);
+      kb = reinterpret_cast<const char*>(p.k) + ((int64_t)page * p.k_sp + (int64_t)slot * p.k_ss + (int64_t)s.g * p.k_sh) * ELT;
+      vb = reinterpret_cast<const char*>(p.v) + ((int64_t)page * p.v_sp + (int64_t)slot * p.v_ss + (int64_t)s.g * p.v_sh) * ELT;
+    }
+  }
+  __device__ __forceinline__ const char* krow(const KParams& p, const SeqCtx& s, int kt) const {
+    const int kk = min(kt, nvalid - 1);
+    if constexpr (FAST) {
+      return kb + (uint32_t)kk * kss;
+    } else {
+      const int key = J0 + kk;
+      const int page = page_of(p, s, key);
+      return reinterpret_cast<const char*>(p.k) +
+             ((int64_t)page * p.k_sp + (int64_t)(key & (p.page_size - 1)) * p.k_ss + (int64_t)s.g * p.k_sh) * ELT;
+    }
+  }
+  __device__ __forceinline__ const char* vrow(const KParams& p, const SeqCtx& s, int kt) const {
+    const int kk = min(kt, nvalid - 1);
+    if constexpr (FAST) {
+      return vb + (uint32_t)kk * vss;
+    } else {
+      const int key = J0 + kk;
+      const int page = page_of(p, s, key);
+      return reinterpret_cast<const char*>(p.v) +
+             ((int64_t)page * p.v_sp + (int64_t)(key & (p.page_size - 1)) * p.v_ss + (int64_t)s.g * p.v_sh) * ELT;
+    }
+  }
+};
+
+template <int KIND>
+__device__ __forceinline__ float kscale_of(const KParams& p, const SeqCtx& s, int key, float* vsc) {
+  if constexpr (KIND != KIND_F8) {
+    *vsc = 1.f;
+    return 1.f;
+  } else {
+    if (p.scale_mode == 2) {              // per (physical page, kv head); page_size >= 64
+      const int page = page_of(p, s, key);
+      *vsc = p.v_scale[page * p.Hkv + s.g];
+      return p.k_scale[page * p.Hkv + s.g];
+    }
+    *vsc = p.v_scale[0];
+    return p.k_scale[0];
+  }
+}
+
+// Q / K row -> QK operands of this lane (group h): K-step ks holds dims
+// 32 ks + 8 h .. +7 (bf16, fp8) or 16 (ks / 4) + 4 h + ks % 4 (fp32).
+template <int KIND, int D>
+__device__ __forceinline__ void load_qk_row(const char* row, int h,
+                                            typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
+  using C = Cfg<KIND, D>;
+  if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks) {
+      u32x4 v = row ? *reinterpret_cast<const u32x4*>(row + (32 * ks + 8 * h) * 2) : u32x4{0, 0, 0, 0};
+      op[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  } else if constexpr (KIND == KIND_F8) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks)
+      op[ks] = row ? *reinterpret_cast<const long*>(row + 32 * ks + 8 * h) : 0L;
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      f32x4 v = row ? *reinterpret_cast<const f32x4*>(row + (16 * c + 4 * h) * 4) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) op[4 * c + i] = v[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// masking of one S^T tile held by a lane: keys J0 + 16 mb + 4 h + j, query row
+// at absolute position `pos`.
+// ---------------------------------------------------------------------------
+struct RowMask {
+  int pos, left;    // causal bound and window start of this lane's row
+  bool bit;         // block-mask bit of (row's query tile, the unit's key tile)
+};
+
+__device__ __forceinline__ bool key_visible(const KParams& p, const RowMask& r, int ctx, int key) {
+  bool v = key < ctx;
+  if (p.causal) v = v && key <= r.pos;
+  if (p.window > 0) v = v && key >= r.left;
+  if (p.landmark > 0) v = v && ((key + 1) % p.landmark) != 0;
+  return v && r.bit;
+}
+
+// The unit needs no per-element mask for any row of [pos_min, pos_max].
+__device__ __forceinline__ bool unit_is_full(const KParams& p, int J0, int ctx, int pos_min,
+                                             int left_max) {
+  if (J0 + 63 >= ctx) return false;
+  if (p.causal && J0 + 63 > pos_min) return false;
+  if (p.window > 0 && J0 < left_max) return false;
+  if (p.landmark > 0) {
+    const int r0 = p.landmark - 1 - (J0 % p.landmark);     // first landmark offset in the tile
+    if (r0 < 64) return false;
+  }
+  if (p.bm) return false;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// online-softmax state of NB row-blocks of one wave
+// ---------------------------------------------------------------------------
+template <int KIND, int D, int NB>
+struct WaveState {
+  f32x4 acc[NB][Cfg<KIND, D>::MD];
+  float m2[NB];       // running max of log2-domain scores of this lane's row
+  float lsum[NB];     // this lane's share of the running sum (reduced at the end)
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m2[nb] = kNegInf;
+      lsum[nb] = 0.f;
+#pragma unroll
+      for (int md = 0; md < Cfg<KIND, D>::MD; ++md) acc[nb][md] = f32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// Softmax update of one row-block: s2 holds log2-domain scores (masked = -inf)
+// and is overwritten by the probabilities.
+template <int KIND, int D, int NB>
+__device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int nb, f32x4 (&s2)[4]) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s2[mb][j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m2[nb], mx);
+  const bool dead = m_new == kNegInf;                   // nothing visible so far
+  const float alpha = dead ? 1.f : __builtin_amdgcn_exp2f(st.m2[nb] - m_new);
+  const float mref = dead ? 0.f : m_new;
+  float sum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(s2[mb][j] - mref);
+      s2[mb][j] = e;
+      sum += e;
+    }
+  st.lsum[nb] = st.lsum[nb] * alpha + sum;
+  st.m2[nb] = m_new;
+#pragma unroll
+  for (int md = 0; md < Cfg<KIND, D>::MD; ++md) st.acc[nb][md] *= alpha;
+}
+
+// P^T operand (bf16) of PV K-step ks2: slot t = key 32 ks2 + 16 (t / 4) + 4 h + t % 4.
+__device__ __forceinline__ bf16x8 p_operand(const f32x4 (&pr)[4], int ks2, float vsc) {
+  u32x4 w;
+  w[0] = pack_bf16x2(pr[2 * ks2][0] * vsc, pr[2 * ks2][1] * vsc);
+  w[1] = pack_bf16x2(pr[2 * ks2][2] * vsc, pr[2 * ks2][3] * vsc);
+  w[2] = pack_bf16x2(pr[2 * ks2 + 1][0] * vsc, pr[2 * ks2 + 1][1] * vsc);
+  w[3] = pack_bf16x2(pr[2 * ks2 + 1][2] * vsc, pr[2 * ks2 + 1][3] * vsc);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// V^T operand for element md from the 8 V row pieces of one PV K-step
+// (index half * 4 + j, each MD bf16 = MD / 2 words): slot t <- piece t, element md.
+template <int MD>
+__device__ __forceinline__ bf16x8 v_operand(const unsigned (&vr)[8][MD / 2], int md) {
+  u32x4 w;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const unsigned a = vr[2 * u][md >> 1], b = vr[2 * u + 1][md >> 1];
+    w[u] = (md & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// A raw V piece: MD consecutive elements of one V row (16 B of bf16 or 8 B of
+// fp8 for d = 128), converted to bf16 words only when the PV operand is built.
+template <int KIND, int MD> struct VRawT;
+template <> struct VRawT<KIND_BF16, 8> { using T = u32x4; };
+template <> struct VRawT<KIND_BF16, 4> { using T = u32x2; };
+template <> struct VRawT<KIND_F8, 8> { using T = u32x2; };
+template <> struct VRawT<KIND_F8, 4> { using T = unsigned; };
+
+template <int KIND, int MD>
+__device__ __forceinline__ typename VRawT<KIND, MD>::T load_v_raw(const char* row, int e0) {
+  return *reinterpret_cast<const typename VRawT<KIND, MD>::T*>(row + e0 * (KIND == KIND_BF16 ? 2 : 1));
+}
+
+template <int KIND, int MD>
+__device__ __forceinline__ void v_words(const typename VRawT<KIND, MD>::T& r, unsigned (&out)[MD / 2]) {
+  if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+    for (int i = 0; i < MD / 2; ++i) out[i] = r[i];
+  } else if constexpr (MD == 8) {
+    out[0] = f8x2_to_bf16x2(r[0]);
+    out[1] = f8x2_to_bf16x2(r[0] >> 16);
+    out[2] = f8x2_to_bf16x2(r[1]);
+    out[3] = f8x2_to_bf16x2(r[1] >> 16);
+  } else {
+    out[0] = f8x2_to_bf16x2(r);
+    out[1] = f8x2_to_bf16x2(r >> 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// final write of one lane's row: O = acc / l (out dtype) and LSE; or the
+// normalised partial (fp32) and its LSE into a slot.  `o` holds the lane's
+// MD x 4 values in accumulator order.
+// ---------------------------------------------------------------------------
+template <int KIND, int D>
+__device__ __forceinline__ int out_dim(int h, int j, int md) {
+  if constexpr (KIND == KIND_F32) return 4 * (4 * h + j) + (md & 3) + 64 * (md >> 2);
+  else return Cfg<KIND, D>::MD * (4 * h + j) + md;
+}
+
+template <int KIND, int D>
+__device__ __forceinline__ void write_row(const KParams& p, const QBlock& x, int r, int h,
+                                          const f32x4 (&acc)[Cfg<KIND, D>::MD], float inv_l,
+                                          float lse, bool final_out, int slot) {
+  constexpr int MD = Cfg<KIND, D>::MD;
+  const int tok = x.q0 + x.t0 + r / p.G, head = x.g * p.G + r % p.G;
+  if (final_out) {
+    if constexpr (KIND == KIND_F32) {
+      float* o = reinterpret_cast<float*>(p.out) + tok * p.o_st + head * p.o_sh;
+#pragma unroll
+      for (int gd = 0; gd < D / 64; ++gd)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[4 * gd + i][j] * inv_l;
+          *reinterpret_cast<f32x4*>(o + out_dim<KIND, D>(h, j, 4 * gd)) = v;
+        }
+    } else {
+      char* o = reinterpret_cast<char*>(p.out) + (tok * p.o_st + head * p.o_sh) * 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        unsigned w[MD / 2];
+#pragma unroll
+        for (int i = 0; i < MD / 2; ++i) w[i] = pack_bf16x2(acc[2 * i][j] * inv_l, acc[2 * i + 1][j] * inv_l);
+        char* dst = o + out_dim<KIND, D>(h, j, 0) * 2;
+        if constexpr (MD == 8) *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+      }
+    }
+    if (h == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
+  } else {
+    float* o = p.part_o + ((int64_t)slot * kLargeRows + r) * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[out_dim<KIND, D>(h, j, md)] = acc[md][j] * inv_l;
+    if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// active-tile list of a block-sparse Q-block (wave 0 builds, all wait):
+// list[i] = tile of active unit u_start + i, for i < n.
+// ---------------------------------------------------------------------------
+__device__ void build_tile_list(const KParams& p, const QBlock& x, int t_lo, int t_hi, int u_start,
+                                int n, short* list) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int rank0 = 0;
+    for (int base = t_lo; base <= t_hi && rank0 < u_start + n; base += 64) {
+      const int t = base + lane;
+      const bool act = t <= t_hi && mask_union(p, x.b, x.g, x.pos_lo, x.pos_hi, t);
+      const unsigned long long bal = __ballot(act);
+      const int rank = rank0 + __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+      if (act && rank >= u_start && rank < u_start + n) list[rank - u_start] = (short)t;
+      rank0 += __popcll(bal);
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// small Q-blocks (<= 16 rows): one wave runs a contiguous run of units with
+// operands loaded straight from HBM into registers, as a rolling pipeline:
+// the K loads of tile u+1 are issued as soon as S(u) has consumed K(u), and
+// its V loads as soon as PV(u) has consumed V(u), so every wave always has
+// about one tile of loads in flight.
+// ---------------------------------------------------------------------------
+template <int KIND, int D>
+struct SmallRegs {
+  using C = Cfg<KIND, D>;
+  static constexpr int MD = C::MD;
+  typename QKOpT<KIND>::T kA[4][C::KSQ];
+  // bf16 / fp8: V row pieces per PV K-step (ks2) and piece (half * 4 + j)
+  typename std::conditional<KIND == KIND_F32, int, typename VRawT<KIND == KIND_F32 ? KIND_BF16 : KIND, MD>::T>::type
+      vr[KIND == KIND_F32 ? 1 : 2][KIND == KIND_F32 ? 1 : 8];
+  // fp32: V rows (mb, j), dims 64 gd + 4 n
+  f32x4 vf[KIND == KIND_F32 ? 4 : 1][KIND == KIND_F32 ? 4 : 1][KIND == KIND_F32 ? D / 64 : 1];
+};
+
+template <int KIND, int D, bool FAST>
+__device__ __forceinline__ void small_load_k(const KParams& p, const SeqCtx& s, const Tile<Cfg<KIND, D>::ELT, FAST>& t,
+                                             SmallRegs<KIND, D>& r, int n, int h) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) load_qk_row<KIND, D>(t.krow(p, s, 16 * mb + n), h, r.kA[mb]);
+}
+
+template <int KIND, int D, bool FAST>
+__device__ __forceinline__ void small_load_v(const KParams& p, const SeqCtx& s, const Tile<Cfg<KIND, D>::ELT, FAST>& t,
+                                             SmallRegs<KIND, D>& r, int n, int h) {
+  constexpr int MD = Cfg<KIND, D>::MD;
+  if constexpr (KIND == KIND_F32) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const char* row = t.vrow(p, s, 16 * mb + 4 * h + j);
+#pragma unroll
+        for (int gd = 0; gd < D / 64; ++gd) r.vf[mb][j][gd] = *reinterpret_cast<const f32x4*>(row + (64 * gd + 4 * n) * 4);
+      }
+  } else {
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc)
+        r.vr[ks2][pc] = load_v_raw<KIND, MD>(t.vrow(p, s, 32 * ks2 + 16 * (pc >> 2) + 4 * h + (pc & 3)), MD * n);
+  }
+}
+
+template <int KIND, int D, bool FAST>
+__device__ __forceinline__ void small_run(const KParams& p, const SeqCtx& s, const QBlock& x, const short* list,
+                                          int c0, int t_lo, int a, int b,
+                                          const typename QKOpT<KIND>::T (&qB)[Cfg<KIND, D>::KSQ], RowMask rm,
+                                          int bm_head, int pos_min, int left_max, WaveState<KIND, D, 1>& st,
+                                          int lane) {
+  using C = Cfg<KIND, D>;
+  constexpr int MD = C::MD;
+  const int n = lane & 15, h = lane >> 4;
+  auto tile_of = [&](int u) { return p.bm ? (int)list[u - c0] : t_lo + u; };
+  Tile<C::ELT, FAST> tc;
+  tc.init(p, s, tile_of(a));
+  SmallRegs<KIND, D> r;
+  small_load_k<KIND, D, FAST>(p, s, tc, r, n, h);
+  small_load_v<KIND, D, FAST>(p, s, tc, r, n, h);
+  for (int u = a; u < b; ++u) {
+    const bool more = u + 1 < b;
+    Tile<C::ELT, FAST> tn = tc;
+    if (more) tn.init(p, s, tile_of(u + 1));
+    const int J0 = tc.J0;
+    float vsc;
+    const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
+    if (p.bm) {
+      const int kt = J0 / p.bm_tile, qt = rm.pos / p.bm_tile;
+      rm.bit = kt < p.bm_nk && qt < p.bm_nq &&
+               p.bm[x.b * p.bm_sb + bm_head * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+    }
+    // S^T = K Q^T
+    f32x4 sc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      sc[mb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < C::KSQ; ++ks) sc[mb] = mfma_qk(r.kA[mb][ks], qB[ks], sc[mb]);
+    }
+    if (more) small_load_k<KIND, D, FAST>(p, s, tn, r, n, h);
+    const bool full = unit_is_full(p, J0, s.ctx, pos_min, left_max);
+    float cs = p.sm_log2;
+    if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = sc[mb][j] * cs;
+        if (!full && !key_visible(p, rm, s.ctx, J0 + 16 * mb + 4 * h + j)) v = kNegInf;
+        sc[mb][j] = v;
+      }
+    softmax_update<KIND, D, 1>(st, 0, sc);
+    // O^T += V^T P^T
+    if constexpr (KIND == KIND_F32) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int md = 0; md < MD; ++md)
+            st.acc[0][md] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.vf[mb][j][md >> 2][md & 3], sc[mb][j],
+                                                                  st.acc[0][md], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        unsigned w[8][MD / 2];
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) v_words<KIND, MD>(r.vr[ks2][pc], w[pc]);
+        const bf16x8 pb = p_operand(sc, ks2, vsc);
+#pragma unroll
+        for (int md = 0; md < MD; ++md) st.acc[0][md] = mfma_pv(v_operand<MD>(w, md), pb, st.acc[0][md]);
+      }
+    }
+    if (more) small_load_v<KIND, D, FAST>(p, s, tn, r, n, h);
+    tc = tn;
+  }
+}
+
+template <int KIND, int D, bool FAST>
+__device__ void small_segment(const KParams& p, const QBlock& x, int t_lo, int t_hi, int u0, int u1,
+                              bool final_out, int slot, char* smem) {
+  using C = Cfg<KIND, D>;
+  constexpr int MD = C::MD;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, h = lane >> 4;
+  short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
+
+  SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
+  // this lane's query row
+  const bool row_ok = n < x.rows;
+  const int r = row_ok ? n : 0;
+  const int tok = x.q0 + x.t0 + r / p.G, head = x.g * p.G + r % p.G;
+  typename QKOpT<KIND>::T qB[C::KSQ];
+  load_qk_row<KIND, D>(row_ok ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
+                              : nullptr, h, qB);
+  RowMask rm;
+  rm.pos = x.ctx - x.ql + x.t0 + r / p.G;
+  rm.left = p.window > 0 ? window_left(p, rm.pos) : 0;
+  rm.bit = true;
+  const int pos_min = x.pos_lo;
+  const int left_max = p.window > 0 ? window_left(p, x.pos_hi) : 0;
+  const int bm_head = p.bm && p.bm_heads != 1 ? head : 0;
+
+  WaveState<KIND, D, 1> st;
+  st.init();
+  // units are taken in chunks of at most kMaskListCap (the list capacity);
+  // inside a chunk the waves take contiguous quarter runs
+  for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
+    const int cn = min(kMaskListCap, u1 - c0);
+    if (p.bm) build_tile_list(p, x, t_lo, t_hi, c0, cn, list);
+    const int a = c0 + (cn * wave) / kWaves, b = c0 + (cn * (wave + 1)) / kWaves;
+    if (a < b) small_run<KIND, D, FAST>(p, s, x, list, c0, t_lo, a, b, qB, rm, bm_head, pos_min, left_max, st, lane);
+    if (p.bm) __syncthreads();                 // list reuse
+  }
+
+  // merge the four waves' states through LDS: m, l per row; acc per row x dims
+  float l = st.lsum[0];
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float* mrg = reinterpret_cast<float*>(smem);
+  float* ms = mrg;                                     // [wave][16]
+  float* ls = mrg + kWaves * 16;                       // [wave][16]
+  float* os = mrg + 2 * kWaves * 16;                   // [wave][16][D]
+  if (h == 0) {
+    ms[wave * 16 + n] = st.m2[0];
+    ls[wave * 16 + n] = l;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int md = 0; md < MD; ++md) os[(wave * 16 + n) * D + out_dim<KIND, D>(h, j, md)] = st.acc[0][md][j];
+  __syncthreads();
+  // thread -> (row, 8 dims)
+  constexpr int TPR = D / 8;                           // threads per row
+  for (int idx = threadIdx.x; idx < 16 * TPR; idx += kThreads) {
+    const int row = idx / TPR, d0 = (idx % TPR) * 8;
+    if (row >= x.rows) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ms[w * 16 + row]);
+    float L = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float c = __builtin_amdgcn_exp2f(ms[w * 16 + row] - M);
+        L += ls[w * 16 + row] * c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] += os[(w * 16 + row) * D + d0 + i] * c;
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const float lse = empty ? kNegInf : (M + log2f(L)) * kLn2;
+    const int tk = x.q0 + x.t0 + row / p.G, hd = x.g * p.G + row % p.G;
+    if (final_out) {
+      if constexpr (KIND == KIND_F32) {
+        float* dst = reinterpret_cast<float*>(p.out) + tk * p.o_st + hd * p.o_sh + d0;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      } else {
+        char* dst = reinterpret_cast<char*>(p.out) + (tk * p.o_st + hd * p.o_sh + d0) * 2;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                                               pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+      }
+      if (d0 == 0) p.lse[tk * p.l_st + hd * p.l_sh] = lse;
+    } else {
+      float* dst = p.part_o + ((int64_t)slot * kLargeRows + row) * D + d0;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// large Q-blocks (up to 128 rows): K/V tiles staged by the whole workgroup
+// into LDS in MFMA-operand order, double-buffered; wave w owns rows 32 w ..
+// ---------------------------------------------------------------------------
+template <int KIND, int D, bool FAST>
+struct Stage {
+  using C = Cfg<KIND, D>;
+  static constexpr int MD = C::MD;
+  // per thread staging registers
+  static constexpr int KCH = KIND == KIND_F32 ? (4 * (D / 16) * 64) / kThreads : (4 * C::KSQ * 64) / kThreads;
+  static constexpr int VCH = KIND == KIND_F32 ? (16 * (D / 64) * 64) / kThreads : 4;
+  using KReg = typename std::conditional<KIND == KIND_F32 || KIND == KIND_BF16, u32x4, u32x2>::type;
+  KReg kr[KCH];
+  u32x4 vf[KIND == KIND_F32 ? VCH : 1];
+  typename VRawT<KIND == KIND_F32 ? KIND_BF16 : KIND, MD>::T vraw[KIND == KIND_F32 ? 1 : 4];
+
+  // global -> registers for the given tile
+  __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile) {
+    Tile<C::ELT, FAST> t;
+    t.init(p, s, tile);
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = i * kThreads + tid;
+      const int ln = c & 63, mk = c >> 6;
+      const int m = ln & 15, hh = ln >> 4;
+      if constexpr (KIND == KIND_F32) {
+        const int mb = mk / (D / 16), cc = mk % (D / 16);
+        kr[i] = *reinterpret_cast<const u32x4*>(t.krow(p, s, 16 * mb + m) + (16 * cc + 4 * hh) * 4);
+      } else {
+        const int mb = mk / C::KSQ, ks = mk % C::KSQ;
+        const char* row = t.krow(p, s, 16 * mb + m);
+        if constexpr (KIND == KIND_BF16) kr[i] = *reinterpret_cast<const u32x4*>(row + (32 * ks + 8 * hh) * 2);
+        else kr[i] = *reinterpret_cast<const u32x2*>(row + 32 * ks + 8 * hh);
+      }
+    }
+    if constexpr (KIND == KIND_F32) {
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int c = i * kThreads + tid;
+        const int ln = c & 63, grp = c >> 6;            // grp = (mb * 4 + j) * (D / 64) + gd
+        const int gd = grp % (D / 64), mbj = grp / (D / 64);
+        const int mb = mbj >> 2, j = mbj & 3;
+        const int m = ln & 15, hh = ln >> 4;
+        vf[i] = *reinterpret_cast<const u32x4*>(t.vrow(p, s, 16 * mb + 4 * hh + j) + (64 * gd + 4 * m) * 4);
+      }
+    } else {
+      // thread -> (ks2, lane_t, half); 4 rows j = 0..3
+      const int task = tid >> 1, half = tid & 1;
+      const int ks2 = task >> 6, ln = task & 63;
+      const int m = ln & 15, hh = ln >> 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vraw[j] = load_v_raw<KIND, MD>(t.vrow(p, s, 32 * ks2 + 16 * half + 4 * hh + j), MD * m);
+    }
+  }
+
+  // registers -> LDS buffer
+  __device__ __forceinline__ void store(char* kbuf, char* vbuf) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = i * kThreads + tid;
+      *reinterpret_cast<KReg*>(kbuf + c * sizeof(KReg)) = kr[i];
+    }
+    if constexpr (KIND == KIND_F32) {
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int c = i * kThreads + tid;
+        *reinterpret_cast<u32x4*>(vbuf + c * 16) = vf[i];
+      }
+    } else {
+      const int task = tid >> 1, half = tid & 1;
+      const int ks2 = task >> 6, ln = task & 63;
+      unsigned vb[4][MD / 2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v_words<KIND, MD>(vraw[j], vb[j]);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const unsigned a0 = vb[0][md >> 1], a1 = vb[1][md >> 1], a2 = vb[2][md >> 1], a3 = vb[3][md >> 1];
+        u32x2 w;
+        if (md & 1) {
+          w[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+          w[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+        } else {
+          w[0] = (a0 & 0xFFFFu) | (a1 << 16);
+          w[1] = (a2 & 0xFFFFu) | (a3 << 16);
+        }
+        *reinterpret_cast<u32x2*>(vbuf + ((ks2 * MD + md) * 64 + ln) * 16 + 8 * half) = w;
+      }
+    }
+  }
+};
+
+template <int KIND, int D, bool FAST>
+__device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t_hi, int u0, int u1,
+                              bool final_out, int slot, char* smem) {
+  using C = Cfg<KIND, D>;
+  constexpr int MD = C::MD;
+  constexpr int NB = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, h = lane >> 4;
+  short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
+  SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
+
+  // this lane's two rows
+  typename QKOpT<KIND>::T qB[NB][C::KSQ];
+  RowMask rm[NB];
+  int rowi[NB];
+  bool rok[NB];
+  int bm_head[NB];
+  int pos_min = 0x7fffffff, left_max = 0;
+  const bool wave_live = 32 * wave < x.rows;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = 32 * wave + 16 * nb + n;
+    rok[nb] = r < x.rows;
+    rowi[nb] = rok[nb] ? r : 0;
+    const int tok = x.q0 + x.t0 + rowi[nb] / p.G, head = x.g * p.G + rowi[nb] % p.G;
+    load_qk_row<KIND, D>(rok[nb] ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
+                                 : nullptr, h, qB[nb]);
+    rm[nb].pos = x.ctx - x.ql + x.t0 + rowi[nb] / p.G;
+    rm[nb].left = p.window > 0 ? window_left(p, rm[nb].pos) : 0;
+    rm[nb].bit = true;
+    bm_head[nb] = p.bm && p.bm_heads != 1 ? head : 0;
+  }
+  if (wave_live) {
+    // bounds over this wave's valid rows (uniform across the wave)
+    const int r_lo = 32 * wave, r_hi = min(x.rows, 32 * wave + 32) - 1;
+    pos_min = x.ctx - x.ql + x.t0 + r_lo / p.G;
+    const int pos_hi_w = x.ctx - x.ql + x.t0 + r_hi / p.G;
+    left_max = p.window > 0 ? window_left(p, pos_hi_w) : 0;
+  }
+
+  WaveState<KIND, D, NB> st;
+  st.init();
+  Stage<KIND, D, FAST> stg;
+
+  for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
+    const int cn = min(kMaskListCap, u1 - c0);
+    if (p.bm) build_tile_list(p, x, t_lo, t_hi, c0, cn, list);
+    auto tile_of = [&](int u) { return p.bm ? (int)list[u - c0] : t_lo + u; };
+    stg.load(p, s, tile_of(c0));
+    stg.store(smem, smem + C::K_TILE);
+    __syncthreads();
+    for (int u = c0; u < c0 + cn; ++u) {
+      const int buf = (u - c0) & 1;
+      char* kbuf = smem + buf * C::STAGE;
+      char* vbuf = kbuf + C::K_TILE;
+      const bool more = u + 1 < c0 + cn;
+      if (more) stg.load(p, s, tile_of(u + 1));
+      const int tile = tile_of(u);
+      const int J0 = tile * kUnitKeys;
+      if (wave_live) {
+        float vsc;
+        const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
+        float cs = p.sm_log2;
+        if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
+        if (p.bm) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int kt = J0 / p.bm_tile, qt = rm[nb].pos / p.bm_tile;
+            rm[nb].bit = kt < p.bm_nk && qt < p.bm_nq &&
+                         p.bm[x.b * p.bm_sb + bm_head[nb] * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+          }
+        }
+        const bool full = unit_is_full(p, J0, x.ctx, pos_min, left_max);
+        // S^T = K Q^T
+        f32x4 sc[NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) sc[nb][mb] = f32x4{0, 0, 0, 0};
+        if constexpr (KIND == KIND_F32) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int cc = 0; cc < D / 16; ++cc) {
+              const f32x4 ka = *reinterpret_cast<const f32x4*>(kbuf + ((mb * (D / 16) + cc) * 64 + lane) * 16);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka[i], qB[nb][4 * cc + i], sc[nb][mb]);
+            }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < C::KSQ; ++ks) {
+              typename QKOpT<KIND>::T ka;
+              if constexpr (KIND == KIND_BF16)
+                ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + ((mb * C::KSQ + ks) * 64 + lane) * 16));
+              else
+                ka = *reinterpret_cast<const long*>(kbuf + ((mb * C::KSQ + ks) * 64 + lane) * 8);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float v = sc[nb][mb][j] * cs;
+              if (!full && !key_visible(p, rm[nb], x.ctx, J0 + 16 * mb + 4 * h + j)) v = kNegInf;
+              sc[nb][mb][j] = v;
+            }
+          softmax_update<KIND, D, NB>(st, nb, sc[nb]);
+        }
+        // O^T += V^T P^T
+        if constexpr (KIND == KIND_F32) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int gd = 0; gd < D / 64; ++gd) {
+                const f32x4 va = *reinterpret_cast<const f32x4*>(vbuf + ((((mb * 4 + j) * (D / 64)) + gd) * 64 + lane) * 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                  for (int nb = 0; nb < NB; ++nb)
+                    st.acc[nb][4 * gd + i] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], sc[nb][mb][j], st.acc[nb][4 * gd + i], 0, 0, 0);
+              }
+        } else {
+#pragma unroll
+          for (int ks2 = 0; ks2 < 2; ++ks2) {
+            bf16x8 pb[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) pb[nb] = p_operand(sc[nb], ks2, vsc);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+              const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vbuf + ((ks2 * MD + md) * 64 + lane) * 16));
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) st.acc[nb][md] = mfma_pv(va, pb[nb], st.acc[nb][md]);
+            }
+          }
+        }
+      }
+      if (more) {
+        char* nk = smem + (buf ^ 1) * C::STAGE;
+        stg.store(nk, nk + C::K_TILE);
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue: per lane row, reduce l over the four lane groups and write
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float l = st.lsum[nb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!rok[nb]) continue;
+    const bool empty = !(l > 0.f);
+    const float inv = empty ? 0.f : 1.f / l;
+    const float lse = empty ? kNegInf : (st.m2[nb] + log2f(l)) * kLn2;
+    write_row<KIND, D>(p, x, rowi[nb], h, st.acc[nb], inv, lse, final_out, slot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the persistent kernel
+// ---------------------------------------------------------------------------
+template <int KIND, int D, bool FAST>
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(KParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int U = p.hdr[H_U];
+  const int L = p.hdr[H_L];
+  const int n_workers = p.hdr[H_NWORKERS];
+  if (U == 0 || n_workers == 0) return;
+  // XCD-aware: consecutive workgroup ids land on different XCDs, so give each
+  // XCD a contiguous block of workers (neighbouring units share K/V in its L2)
+  const int G8 = gridDim.x / 8;
+  const int rank = (gridDim.x % 8 == 0) ? (blockIdx.x % 8) * G8 + blockIdx.x / 8 : blockIdx.x;
+  const int n_qb = p.hdr[H_NQB];
+  for (int vw = rank; vw < n_workers; vw += gridDim.x) {
+    int a = vw * L;
+    const int b_end = min(a + L, U);
+    // Q-block containing unit a: last q with unit_prefix[q] <= a
+    int lo = 0, hi = n_qb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.unit_prefix[mid] <= a) lo = mid; else hi = mid - 1;
+    }
+    int q = lo;
+    while (a < b_end && q < n_qb) {
+      const int S = p.unit_prefix[q], nq = p.unit_prefix[q + 1] - S;
+      if (nq == 0) { ++q; continue; }
+      const int u0 = a - S, u1 = min(b_end, S + nq) - S;
+      const QBlock x = load_qblock(p, q);
+      int t_lo = 0, t_hi = 0;
+      qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, t_lo, t_hi);
+      const bool final_out = p.n_splits[q] == 1;
+      const int slot = final_out ? 0 : p.slot_base[q] + (vw - S / L);
+      if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(p, x, t_lo, t_hi, u0, u1, final_out, slot, smem);
+      else large_segment<KIND, D, FAST>(p, x, t_lo, t_hi, u0, u1, final_out, slot, smem);
+      a = S + u1;
+      ++q;
+    }
+  }
+}
+
+template <int KIND, int D, bool FAST>
+static hipError_t launch_attention_t(const KParams& p, int grid, hipStream_t stream) {
+  const int lds = Cfg<KIND, D>::LDS;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL((attention_kernel<KIND, D, FAST>), dim3(grid), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int KIND, int D>
+static hipError_t launch_attention_kd(const KParams& p, int grid, hipStream_t stream) {
+  return p.page_size >= kUnitKeys ? launch_attention_t<KIND, D, true>(p, grid, stream)
+                                  : launch_attention_t<KIND, D, false>(p, grid, stream);
+}
+
+hipError_t launch_attention(const KParams& p, int kind, int grid, hipStream_t stream) {
+  if (kind == KIND_F32) return p.D == 64 ? launch_attention_kd<KIND_F32, 64>(p, grid, stream)
+                                         : launch_attention_kd<KIND_F32, 128>(p, grid, stream);
+  if (kind == KIND_BF16) return p.D == 64 ? launch_attention_kd<KIND_BF16, 64>(p, grid, stream)
+                                          : launch_attention_kd<KIND_BF16, 128>(p, grid, stream);
+  return p.D == 64 ? launch_attention_kd<KIND_F8, 64>(p, grid, stream)
+                   : launch_attention_kd<KIND_F8, 128>(p, grid, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,118 @@
+// pa_device.h — kernel parameter block and the integer rules of the work split,
+// shared by the Assign, attention and Combine kernels of libpaged_attn.
+//
+// The split follows "Triton-TLE rewrite of Tencent HPC-Ops Attention", §1.2
+// (Assign cuts every KV sequence into tiles and balances the tiles over
+// persistent workgroups; Split-K emits partial output + LSE; Combine merges
+// them) and §3.3 (pick the chunk length from the total load, then cut each
+// request by its real KV length; a task owned by one workgroup writes its
+// result directly), with the Q-block grouping of "vLLM Triton Attention
+// Backend Deep Dive", §3 (all query heads of one KV head, several tokens).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kUnitKeys = 64;        // keys per unit (one KV tile)
+constexpr int kSmallMaxRows = 16;    // q_len * G <= 16: one Q-block holds all query tokens of (b, g)
+constexpr int kLargeRows = 128;      // otherwise Q-blocks of 128 / G tokens
+constexpr int kThreads = 256;        // four wave64 per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kHeaderInts = 16;
+constexpr int kMaskListCap = 1024;   // active-tile list entries kept in LDS at once
+
+enum HeaderField {
+  H_U = 0, H_P = 1, H_L = 2, H_NQB = 3, H_NSLOTS = 4, H_NCOMBINE = 5, H_NWORKERS = 6,
+  H_ERROR = 7, H_MAXSLOTS = 8
+};
+
+enum DevError { E_NONE = 0, E_QSL = 1, E_QLEN = 2, E_SLOTS = 3, E_PAGE = 5 };
+
+enum Kind { KIND_F32 = 0, KIND_BF16 = 1, KIND_F8 = 2 };
+
+struct KParams {
+  // inputs (element strides)
+  const void* q;  int64_t q_st, q_sh;
+  const void* k;  int64_t k_sp, k_ss, k_sh;
+  const void* v;  int64_t v_sp, v_ss, v_sh;
+  void* out;      int64_t o_st, o_sh;
+  float* lse;     int64_t l_st, l_sh;
+  const int32_t* bt; int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  const uint8_t* bm; int64_t bm_sb, bm_sh, bm_sq, bm_sk;
+  int32_t bm_heads, bm_nq, bm_nk, bm_tile;
+  const float* q_scale; const float* k_scale; const float* v_scale;
+  int32_t scale_mode;
+  // sizes
+  int32_t B, Hq, Hkv, G, D, page_size, page_shift, num_pages, total_q, max_pages;
+  // scores and masks
+  float sm_log2;     // softmax_scale * log2(e)
+  int32_t causal, window, expand, landmark;
+  // split
+  int32_t P, L_min, force_L, max_slots, n_qb_max;
+  // workspace
+  int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
+  int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;
+  float* part_lse; float* part_o;
+};
+
+// First key a query at `pos` may see under the sliding window.
+__device__ __forceinline__ int window_left(const KParams& p, int pos) {
+  int left = pos - p.window + 1;
+  if (left < 0) left = 0;
+  if (p.expand && p.landmark > 0) left = (left / p.landmark) * p.landmark;
+  return left;
+}
+
+// 64-key tile range [t_lo, t_hi] a Q-block with positions pos_lo..pos_hi may
+// touch; false when it touches none.
+__device__ __forceinline__ bool qblock_tiles(const KParams& p, int ctx, int pos_lo, int pos_hi,
+                                             int& t_lo, int& t_hi) {
+  int hi = p.causal ? min(ctx - 1, pos_hi) : ctx - 1;
+  int lo = p.window > 0 ? window_left(p, pos_lo) : 0;
+  if (hi < lo) return false;
+  t_lo = lo / kUnitKeys;
+  t_hi = hi / kUnitKeys;
+  return true;
+}
+
+// Block-mask test of a 64-key tile for a Q-block: set for some query tile
+// covering pos_lo..pos_hi and some query head of kv head g.
+__device__ __forceinline__ bool mask_union(const KParams& p, int b, int g, int pos_lo, int pos_hi,
+                                           int tile) {
+  const int kt = (tile * kUnitKeys) / p.bm_tile;
+  if (kt >= p.bm_nk) return false;
+  const int qt0 = pos_lo / p.bm_tile;
+  int qt1 = pos_hi / p.bm_tile;
+  if (qt1 >= p.bm_nq) qt1 = p.bm_nq - 1;
+  const int h0 = p.bm_heads == 1 ? 0 : g * p.G;
+  const int h1 = p.bm_heads == 1 ? 1 : (g + 1) * p.G;
+  const uint8_t* base = p.bm + b * p.bm_sb + kt * p.bm_sk;
+  for (int hm = h0; hm < h1; ++hm)
+    for (int qt = qt0; qt <= qt1; ++qt)
+      if (base[hm * p.bm_sh + qt * p.bm_sq]) return true;
+  return false;
+}
+
+// Decoded Q-block: rows are (token t0 + r / G, head g * G + r % G).
+struct QBlock {
+  int b, g, t0, nt, rows, ql, ctx, q0, pos_lo, pos_hi;
+};
+
+__device__ __forceinline__ QBlock load_qblock(const KParams& p, int q) {
+  QBlock x;
+  const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[q];
+  x.b = d.x; x.g = d.y; x.t0 = d.z; x.nt = d.w;
+  x.rows = x.nt * p.G;
+  x.q0 = p.qsl[x.b];
+  x.ql = p.qsl[x.b + 1] - x.q0;
+  x.ctx = p.seq_lens[x.b];
+  x.pos_lo = x.ctx - x.ql + x.t0;
+  x.pos_hi = x.pos_lo + x.nt - 1;
+  return x;
+}
+
+}  // namespace pa

@@ -7,11 +7,13 @@ is the one piece shared by the tests, the benchmark and the oracle checks.
 
 Recipe (common to all workloads)
 * One ``numpy.random.default_rng(seed)`` stream, drawn in the order
-  lengths -> page permutation -> Q -> K -> V -> block mask.  (The MTP decode
-  runs draw Q from a second stream seeded 200 + q_len so that the K/V of one
-  batch are shared by every q_len.)
-* Values are N(0, 1) float32 draws rounded to the stored type by torch's
-  round-to-nearest-even casts.  FP8 (E4M3FN) values are divided by a scale
+  lengths -> page permutation -> value seeds -> block mask.  The N(0, 1)
+  float32 values come from three ``torch.Generator`` streams seeded from it,
+  one each for Q, K and V (K and V drawn sequence by sequence).  (The MTP decode runs seed Q from
+  a second numpy stream seeded 200 + q_len so that the K/V of one batch are
+  shared by every q_len.)
+* Values are rounded to the stored type by torch's round-to-nearest-even
+  casts.  FP8 (E4M3FN) values are divided by a scale
   amax / 448 first (1.0 when amax is 0): one scale per tensor, or for K and V
   one per (physical page, kv head).
 * The physical page pool holds exactly the pages the batch needs unless a
@@ -133,20 +135,25 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
         bt[b, :n_pages_seq[b]] = perm[off:off + n_pages_seq[b]]
         off += n_pages_seq[b]
 
-    # Q
+    # value streams
+    q_seed = int((q_rng or rng).integers(0, 2 ** 62))
+    k_seed = int(rng.integers(0, 2 ** 62))
+    v_seed = int(rng.integers(0, 2 ** 62))
     total_q = sum(q_len)
-    qs = (q_rng or rng).standard_normal((total_q, Hq, d), dtype=np.float32)
+    qs = torch.randn((total_q, Hq, d), generator=torch.Generator().manual_seed(q_seed)).numpy()
     if q_gain != 1.0:
         qs = qs * np.float32(q_gain)
-
-    # K, V (dense per sequence, float32 draws)
-    ks = [rng.standard_normal((c, Hkv, d), dtype=np.float32) for c in ctx]
-    vs = [rng.standard_normal((c, Hkv, d), dtype=np.float32) for c in ctx]
+    k_gen = torch.Generator().manual_seed(k_seed)
+    v_gen = torch.Generator().manual_seed(v_seed)
 
     scales = None
+    ks = vs = None
     if kind == "e4m3":
         if quant_mode not in ("tensor", "page_head"):
             raise ValueError("e4m3 needs quant_mode 'tensor' or 'page_head'")
+        # scales need every value first: draw all K, then all V
+        ks = [torch.randn((c, Hkv, d), generator=k_gen).numpy() for c in ctx]
+        vs = [torch.randn((c, Hkv, d), generator=v_gen).numpy() for c in ctx]
         q_s = _f8_scale(float(np.abs(qs).max()) if qs.size else 0.0)
         if quant_mode == "tensor":
             k_s = _f8_scale(max((float(np.abs(k).max()) for k in ks if k.size), default=0.0))
@@ -171,15 +178,23 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
         q_t = _cast(qs, kind)
 
     shape = (num_pages, page_size, Hkv, d) if kv_layout == "NHD" else (num_pages, Hkv, page_size, d)
-    k_cache = _poison_fill(shape, kind, poison)
-    v_cache = _poison_fill(shape, kind, poison)
+    dt = TORCH_DTYPE[kind]
+    k_cache = torch.empty(shape, dtype=dt)
+    v_cache = torch.empty(shape, dtype=dt)
+    used = np.zeros(num_pages, dtype=bool)
     dense_k, dense_v = ([], []) if keep_dense else (None, None)
     for b in range(B):
         npg = n_pages_seq[b]
+        kb = ks[b] if ks is not None else torch.randn((ctx[b], Hkv, d), generator=k_gen).numpy()
+        vb = vs[b] if vs is not None else torch.randn((ctx[b], Hkv, d), generator=v_gen).numpy()
         if npg == 0:
+            if dense_k is not None:
+                dense_k.append(_cast(kb, kind) if kind != "e4m3" else torch.empty((0, Hkv, d), dtype=dt))
+                dense_v.append(_cast(vb, kind) if kind != "e4m3" else torch.empty((0, Hkv, d), dtype=dt))
             continue
+        used[bt[b, :npg]] = True
         pages = torch.from_numpy(bt[b, :npg].astype(np.int64))
-        for arr, cache, dense, which in ((ks[b], k_cache, dense_k, "k"), (vs[b], v_cache, dense_v, "v")):
+        for arr, cache, dense, which in ((kb, k_cache, dense_k, "k"), (vb, v_cache, dense_v, "v")):
             if kind == "e4m3":
                 if quant_mode == "tensor":
                     stored = _cast(arr, kind, float(scales[which][0]))
@@ -197,6 +212,12 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
             if kv_layout == "HND":
                 padded = padded.transpose(1, 2)
             cache[pages] = padded
+        del kb, vb
+    free = torch.from_numpy(np.nonzero(~used)[0])
+    if free.numel():
+        fill = _poison_fill((free.numel(),) + shape[1:], kind, poison)
+        k_cache[free] = fill
+        v_cache[free] = fill
     del ks, vs
 
     block_mask = None

@@ -1,0 +1,232 @@
+/*
+ * paged_attn.h — C ABI of the MI355X (gfx950) paged-KV attention forward library.
+ *
+ * One call computes, for every query token of a packed varlen batch and every
+ * query head, O = softmax(scale * Q K^T + mask) V over that sequence's keys,
+ * which live in a paged KV cache, plus LSE = ln sum exp(scale * Q K^T) over the
+ * visible keys.  The operation and its pieces are the ones described on the
+ * pages about paged attention:
+ *
+ *  - "Triton-TLE rewrite of Tencent HPC-Ops Attention" (flagos.csdn.net),
+ *    §1.2: dynamic decode in three stages — Assign (cut each KV sequence into
+ *    tiles and build a load-balanced task map), Split-K compute (a persistent
+ *    grid walks the task map and emits a partial output and LSE per KV chunk)
+ *    and Combine (LSE-weighted merge, equal to full attention); prefill with
+ *    QK, causal mask, fp32 online softmax, PV and a normalising epilogue;
+ *    block table lookup of physical pages; 128x128 block-mask tile skipping;
+ *    FP8 (e4m3) K/V with quantisation scales.  §3.2: NHD and HND caches
+ *    differ only in strides over logical (page, slot, head, dim) coordinates.
+ *  - "Chunked Prefill kernel optimisation: Triton hybrid attention" (xdnf.cn):
+ *    a chunk of prefill tokens and many decode rows in one launch; decode rows
+ *    see their whole history, a chunk is causal within itself.
+ *  - "HiLS-Attention sliding-window forward" (flagos.csdn.net), §3: LSE in
+ *    natural log, output layout (B, Hq, Lq, Dv) through strides, sliding
+ *    window with expand_to_chunk and landmark masking (j + 1) mod C != 0,
+ *    split-KV decode.
+ *  - "vLLM Triton Attention Backend Deep Dive" (papercache), §3: Q blocks
+ *    group all query heads of one KV head; a persistent grid of fixed size
+ *    reads its work from GPU metadata (so a launch is graph-capturable).
+ *
+ * Conventions for every entry point
+ *  - Every function returns a pa_status; PA_OK is 0.
+ *  - Device pointers are HIP device memory of the current device; host
+ *    pointers are named *_h.  The library allocates no memory, never
+ *    synchronises, never reads device memory on the host and keeps no pointer
+ *    after a call returns.  The caller owns every buffer, the workspace
+ *    included.  All argument checks run before the first launch: a call that
+ *    fails has no side effects.
+ *  - Calls are re-entrant; two calls that share a workspace must be ordered
+ *    on one stream.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent shape/stride, bad size */
+  PA_ERR_UNSUPPORTED = 2,   /* dtype mix, head_dim, GQA ratio or layout not built */
+  PA_ERR_WORKSPACE = 3,     /* workspace null, misaligned or too small */
+  PA_ERR_HIP = 4            /* a HIP runtime call failed; see paged_attn_last_hip_error */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_BF16 = 1,
+  PA_F8E4M3 = 2,            /* OCP E4M3FN */
+  PA_U8 = 3
+} pa_dtype;
+
+/* A strided view of device memory.  shape/stride are in elements; unused
+ * trailing entries are ignored.  The innermost (last) dimension must have
+ * stride 1 except where noted. */
+typedef struct pa_tensor {
+  void* data;
+  int32_t dtype;            /* pa_dtype */
+  int32_t rank;
+  int64_t shape[4];
+  int64_t stride[4];
+} pa_tensor;
+
+typedef enum pa_scale_mode {
+  PA_SCALE_NONE = 0,
+  PA_SCALE_PER_TENSOR = 1,      /* q_scale, k_scale, v_scale: one fp32 each */
+  PA_SCALE_PER_PAGE_HEAD = 2    /* q_scale: one fp32; k_scale, v_scale: fp32 [num_pages, Hkv] */
+} pa_scale_mode;
+
+/* FP8 dequantisation scales (device pointers, so a call never reads them on
+ * the host and stays capturable in a HIP graph).  Value = e4m3(x) * scale.
+ * Required when Q/K/V are PA_F8E4M3, ignored otherwise. */
+typedef struct pa_scales {
+  int32_t mode;             /* pa_scale_mode */
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+} pa_scales;
+
+typedef struct pa_params {
+  /* sizes; each must agree with the tensors passed to paged_attn_fwd */
+  int32_t num_seqs;             /* B */
+  int32_t num_q_heads;          /* Hq */
+  int32_t num_kv_heads;         /* Hkv; Hq % Hkv == 0 and 128 % (Hq / Hkv) == 0 */
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t page_size;            /* a power of two */
+  int32_t num_pages;            /* physical pages in the cache */
+  int32_t max_pages_per_seq;    /* columns of block_table */
+  int32_t block_table_stride;   /* elements between rows of block_table (>= max_pages_per_seq) */
+  int32_t total_q;              /* query tokens = query_start_loc[B] */
+  /* scores and masking */
+  float softmax_scale;          /* multiplies Q.K (fp32, used as given) */
+  int32_t causal;               /* 1: key j visible only if j <= pos (bottom-right aligned) */
+  int32_t window;               /* > 0: sliding window of this many keys ending at pos */
+  int32_t window_expand_to_chunk; /* 1: window start rounded down to a multiple of landmark_chunk */
+  int32_t landmark_chunk;       /* C > 0: hide keys with (j + 1) % C == 0 */
+  int32_t block_mask_tile;      /* tile edge of block_mask in tokens; multiple of 64; 0 = 128 */
+  /* scheduling */
+  int32_t num_workers;          /* P persistent workgroups; 0 = 2 per compute unit */
+  int32_t split_min_units;      /* L_min: fewest 64-key units a worker is given; 0 = 8 */
+  int32_t force_split_units;    /* > 0: every worker gets exactly this many units (testing) */
+  int32_t max_partial_slots;    /* capacity for split partial outputs; 0 = 2 * P */
+  int32_t flags;                /* reserved, must be 0 */
+} pa_params;
+
+/* Where the Assign task map sits inside a workspace (byte offsets), for tests
+ * that copy the workspace to the host and check the map bit for bit. */
+typedef struct pa_workspace_layout {
+  size_t header;          /* int32[16]: U, P, L, n_qb, n_slots, n_combine, n_workers, error, max_slots */
+  size_t seq_qb_base;     /* int32[B + 1]: first Q-block of each sequence */
+  size_t qb_desc;         /* int32[n_qb_max][4]: b, g, t0, nt */
+  size_t unit_prefix;     /* int32[n_qb_max + 1] */
+  size_t n_splits;        /* int32[n_qb_max] */
+  size_t slot_base;       /* int32[n_qb_max], -1 when not split */
+  size_t combine_list;    /* int32[n_qb_max] */
+  size_t partial_lse;     /* float[max_slots][128] */
+  size_t partial_o;       /* float[max_slots][128][head_dim] */
+  size_t total;           /* bytes needed */
+  int32_t n_qb_max;
+  int32_t max_slots;
+  int32_t num_workers;
+} pa_workspace_layout;
+
+typedef struct pa_device_info {
+  int32_t compute_units;
+  int32_t lds_bytes_per_workgroup;
+  int32_t default_workers;
+  char arch[64];
+} pa_device_info;
+
+/* Error word values written by the device into header[7]. */
+typedef enum pa_device_error {
+  PA_DEV_OK = 0,
+  PA_DEV_BAD_QSL = 1,        /* query_start_loc not a non-decreasing prefix ending at total_q */
+  PA_DEV_BAD_QLEN = 2,       /* some q_len > seq_len */
+  PA_DEV_SLOTS = 3,          /* more split partials than max_partial_slots */
+  PA_DEV_BAD_PAGE = 5        /* a block_table entry needed for a key is outside [0, num_pages) */
+} pa_device_error;
+
+/*
+ * paged_attn_fwd — the whole forward pass, enqueued on `stream` as three
+ * launches: Assign (one workgroup builds the task map in the workspace),
+ * the persistent split-K attention kernel (P workgroups), Combine.
+ *
+ *  q            [total_q, Hq, d], dtype f32 | bf16 | e4m3; strides for the
+ *               first two dims are free (d contiguous).
+ *  k_cache,     logical [num_pages, page_size, Hkv, d] (page, slot, head,
+ *  v_cache      dim) with free strides on the first three dims, so an NHD
+ *               cache [pages, slot, head, d] and an HND cache
+ *               [pages, head, slot, d] are both passed by permuting strides.
+ *               Same dtype as q.  Only slots j < seq_len of each sequence are
+ *               read; other slots may hold anything (NaN included).
+ *  block_table  int32 [B, max_pages_per_seq] (row stride
+ *               params->block_table_stride); entry [b, j / page_size] is the
+ *               physical page of key j of sequence b.  Entries past a
+ *               sequence's last page are never read.
+ *  seq_lens     int32 [B]: keys of each sequence, counting its new tokens.
+ *  query_start_loc int32 [B + 1]: query rows of sequence b are
+ *               [qsl[b], qsl[b+1]); token i of the q_len = qsl[b+1] - qsl[b]
+ *               new tokens sits at position seq_len - q_len + i.
+ *  block_mask   optional (NULL = none) u8 [B, H_m, n_q_tiles, n_k_tiles],
+ *               H_m in {1, Hq}, free strides; tile (pos / T, j / T) with
+ *               T = block_mask_tile must be non-zero for key j to be visible.
+ *               Tiles above the causal diagonal are ignored.
+ *  scales       required for e4m3 inputs, else NULL.
+ *  out          [total_q, Hq, d] f32 for f32 inputs, bf16 otherwise; free
+ *               strides on the first two dims (e.g. (B=1, Hq, Lq, d) storage).
+ *  lse          f32 [total_q, Hq], free strides: natural-log LSE.
+ *               Rows with no visible key get O = 0 and LSE = -inf.
+ *  workspace    device memory of at least paged_attn_workspace_size bytes,
+ *               256-byte aligned; its contents need no initialisation and are
+ *               overwritten (the task map stays there after the call).
+ *  stream       a hipStream_t (NULL = default stream).
+ */
+pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, const pa_tensor* block_mask,
+                         const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
+                         const pa_params* params, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Bytes of workspace paged_attn_fwd needs for `params` (host only; queries the
+ * current device's compute-unit count when params->num_workers is 0). */
+pa_status paged_attn_workspace_size(const pa_params* params, size_t* bytes);
+
+/* Offsets of the task map inside the workspace (host only). */
+pa_status paged_attn_workspace_layout(const pa_params* params, pa_workspace_layout* layout);
+
+/* Host-side check of batch metadata held in host memory: query_start_loc is a
+ * prefix ending at total_q, 0 <= q_len <= seq_len, every block_table entry a
+ * sequence needs is in [0, num_pages), and (when block_mask_h is given, a
+ * dense [B, mask_heads, n_q_tiles, n_k_tiles] array) the mask covers every
+ * sequence.  Runs no device code. */
+pa_status paged_attn_validate_host(const pa_params* params, const int32_t* seq_lens_h,
+                                   const int32_t* query_start_loc_h, const int32_t* block_table_h,
+                                   const uint8_t* block_mask_h, int32_t mask_heads,
+                                   int32_t mask_q_tiles, int32_t mask_k_tiles);
+
+/* Compute units, LDS per workgroup and the default worker count of `device`. */
+pa_status paged_attn_device_info(int32_t device, pa_device_info* info);
+
+/* Static text for a status code. */
+const char* paged_attn_status_string(pa_status status);
+
+/* The last HIP error code seen by the calling thread (0 = none). */
+int32_t paged_attn_last_hip_error(void);
+
+/* Kernel timing for benchmarks: while enabled, every paged_attn_fwd records
+ * HIP events on its own stream around each of its three launches.
+ * paged_attn_kernel_timing_read waits for the recorded events, returns the
+ * summed milliseconds per launch and the number of calls, and clears them. */
+pa_status paged_attn_kernel_timing(int32_t enable);
+pa_status paged_attn_kernel_timing_read(float* ms_assign, float* ms_attention, float* ms_combine,
+                                        int32_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,350 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances (max abs error over every compared element):
+  bf16 inputs  O <= 2e-2, LSE <= 1e-3   (fp32 accumulation, P rounded to bf16)
+  fp8  inputs  O <= 4e-2, LSE <= 1e-3   (against the oracle on dequantised inputs)
+  fp32 inputs  O <= 1e-5, LSE <= 1e-5
+Task-map and index work: bit-exact.  Full-size workloads are compared on
+sampled query rows that the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from attention_paged_kv_attn_amd import binding as B
+from attention_paged_kv_attn_amd import workloads as W
+from oracle import taskmap
+from tests.oracle_helpers import run_oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-3), "e4m3": (4e-2, 1e-3), "f32": (1e-5, 1e-5)}
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(batch, **kw):
+    g = batch.to(DEV)
+    say(f"  launch {batch.name} total_q={batch.total_q} B={batch.num_seqs} kw={kw}")
+    out, lse, ws = B.run_batch(g, **kw)
+    torch.cuda.synchronize()
+    return g, out, lse, ws
+
+
+def header(ws, params):
+    lay = B.paged_attn_workspace_layout(params)
+    h = ws[lay.header:lay.header + 64].cpu().view(torch.int32).numpy()
+    return h, lay
+
+
+def params_of(g, **kw):
+    args = dict(num_seqs=g.num_seqs, num_q_heads=g.num_q_heads, num_kv_heads=g.num_kv_heads,
+                head_dim=g.head_dim, page_size=g.page_size, num_pages=g.num_pages,
+                max_pages_per_seq=g.block_table.shape[1], total_q=g.total_q,
+                softmax_scale=g.softmax_scale, causal=g.causal, window=g.window,
+                window_expand_to_chunk=g.window_expand_to_chunk, landmark_chunk=g.landmark_chunk,
+                block_mask_tile=g.block_mask_tile)
+    args.update(kw)
+    return B.make_params(**args)
+
+
+def compare(batch, out, lse, rows=None, tol=None, **oracle_kw):
+    O, L = run_oracle(batch, rows=rows, **oracle_kw)
+    o = out.float().cpu().numpy()
+    l = lse.float().cpu().numpy()
+    sel = np.ones(batch.total_q, bool) if rows is None else np.asarray(rows)
+    to, tl = tol or TOL[batch.kind]
+    assert np.all(np.isfinite(o[sel])), "non-finite output"
+    eo = np.abs(o[sel] - O[sel]).max()
+    el = np.abs(l[sel] - L[sel]).max()
+    say(f"  {batch.name}: max|dO|={eo:.3e} max|dLSE|={el:.3e} rows={int(sel.sum())}")
+    assert eo <= to, f"O error {eo} > {to}"
+    assert el <= tl, f"LSE error {el} > {tl}"
+    return eo, el
+
+
+def check_no_device_error(ws, g, **kw):
+    h, _ = header(ws, params_of(g, **kw))
+    assert h[7] == 0, f"device error word {h[7]}"
+    return h
+
+
+def oracle_taskmap(b, P, force=0):
+    return taskmap.build(b.seq_lens.numpy(), b.query_start_loc.numpy(), Hq=b.num_q_heads,
+                         Hkv=b.num_kv_heads, num_workers=P, split_min_units=8, force_split_units=force,
+                         causal=b.causal, window=b.window, window_expand_to_chunk=b.window_expand_to_chunk,
+                         landmark_chunk=b.landmark_chunk,
+                         block_mask=None if b.block_mask is None else b.block_mask.numpy(),
+                         block_mask_tile=b.block_mask_tile)
+
+
+def slots_for(b, P, force):
+    """Partial slots a forced split needs (the default 2 P covers natural splits)."""
+    return max(1, oracle_taskmap(b, P, force)["n_slots"]) if force else 0
+
+
+def sample_rows(total_q, k, seed=0, must=()):
+    rng = np.random.default_rng(seed)
+    m = np.zeros(total_q, bool)
+    m[rng.choice(total_q, size=min(k, total_q), replace=False)] = True
+    m[list(must)] = True
+    return m
+
+
+# ---------------------------------------------------------------------------
+def test_device_info():
+    info = B.paged_attn_device_info(0)
+    say(f"  device {info}")
+    assert info["compute_units"] > 0 and "gfx950" in info["arch"]
+
+
+@pytest.mark.parametrize("make", [
+    lambda: W.tiny_hybrid(),
+    lambda: W.splitk_decode(q_len=1, batch=16, ctx_lo=64, ctx_hi=3000),
+    lambda: W.splitk_decode(q_len=[1, 2, 4, 3] * 4, batch=16, ctx_lo=64, ctx_hi=3000),
+    lambda: W.hybrid_chunked(batch=12, chunk=200, history=700, dec_lo=100, dec_hi=2000),
+    lambda: W.sparse_prefill(kind="bf16", seq_len=1024),
+    lambda: W.sliding_window(seq_len=1500, window=512),
+], ids=["tiny", "decode", "mtp_mix", "hybrid", "sparse", "window"])
+@pytest.mark.parametrize("workers,force", [(0, 0), (7, 0), (64, 0), (37, 1), (5, 3)])
+def test_taskmap_bit_exact(make, workers, force):
+    b = make()
+    info = B.paged_attn_device_info(0)
+    P = workers or info["default_workers"]
+    ref = oracle_taskmap(b, P, force)
+    slots = slots_for(b, P, force)
+    g, out, lse, ws = gpu_run(b, num_workers=workers, force_split_units=force, max_partial_slots=slots)
+    params = params_of(g, num_workers=workers, force_split_units=force, max_partial_slots=slots)
+    h, lay = header(ws, params)
+    wsc = ws.cpu()
+    n = ref["n_qb"]
+
+    def arr(off, count, width=1):
+        a = wsc[off:off + 4 * count * width].view(torch.int32).numpy()
+        return a.reshape(-1, width) if width > 1 else a
+
+    assert h[7] == 0
+    assert (h[0], h[1], h[2], h[3], h[4], h[5], h[6]) == (
+        ref["U"], P, ref["L"], n, ref["n_slots"], len(ref["combine_list"]), ref["n_workers"])
+    assert np.array_equal(arr(lay.qb_desc, n, 4), ref["desc"])
+    assert np.array_equal(arr(lay.unit_prefix, n + 1), ref["unit_prefix"])
+    assert np.array_equal(arr(lay.n_splits, n), ref["n_splits"])
+    assert np.array_equal(arr(lay.slot_base, n), ref["slot_base"])
+    assert np.array_equal(arr(lay.combine_list, len(ref["combine_list"])), ref["combine_list"])
+    # and the outputs are right under this split
+    compare(b, out, lse)
+
+
+def test_tiny_hybrid_f32():
+    b = W.tiny_hybrid()
+    P = B.paged_attn_device_info(0)["default_workers"]
+    for kw in ({}, {"force_split_units": 1, "max_partial_slots": slots_for(b, P, 1)}, {"num_workers": 1}):
+        g, out, lse, ws = gpu_run(b, **kw)
+        check_no_device_error(ws, g, **kw)
+        compare(b, out, lse)
+
+
+def test_tiny_hybrid_closed_forms(golden):
+    # Q = 0: LSE = ln(visible keys), O = mean of visible V rows
+    b = W.tiny_hybrid()
+    b.q = torch.zeros_like(b.q)
+    g, out, lse, ws = gpu_run(b)
+    counts = np.array([int(c) for _, c in golden("tiny_hybrid_visible_counts.txt")])
+    assert np.abs(lse.cpu().numpy() - np.log(counts)[:, None]).max() <= 1e-5
+    compare(b, out, lse)
+    # one-hot V: the output row is the probability vector; masked keys get exactly 0
+    b = W.tiny_hybrid()
+    bt = b.block_table.numpy()
+    for s in (0, 2):
+        for j in range(int(b.seq_lens[s])):
+            b.v_cache[bt[s, j // 16], j % 16, 0, :] = 0.0
+            b.v_cache[bt[s, j // 16], j % 16, 0, j] = 1.0
+    g, out, lse, ws = gpu_run(b)
+    o = out.cpu().numpy()
+    for t in range(2, 18):                       # chunk rows: pos = 48 + (t - 2)
+        pos = 48 + (t - 2)
+        assert np.all(o[t, :, pos + 1:] == 0.0)
+    assert np.all(o[0, :, 37:] == 0.0)
+    compare(b, out, lse)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("q_len", [1, 2, 4])
+def test_decode_reduced(q_len, layout):
+    b = W.splitk_decode(q_len=q_len, kv_layout=layout, batch=12, ctx_lo=100, ctx_hi=6000)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+def test_decode_mixed_mtp_and_peaked():
+    b = W.splitk_decode(q_len=[1, 2, 4, 3, 1, 4, 2, 1], batch=8, ctx_lo=64, ctx_hi=5000, q_gain=8.0)
+    g, out, lse, ws = gpu_run(b)
+    compare(b, out, lse)
+
+
+@pytest.mark.parametrize("q_len,layout", [(1, "NHD"), (4, "HND")])
+def test_decode_full_size_sampled(q_len, layout):
+    b = W.splitk_decode(q_len=q_len, kv_layout=layout)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    # all rows of 6 sequences: the shortest, the longest and 4 random ones
+    ctx = b.seq_lens.numpy()
+    seqs = {int(ctx.argmin()), int(ctx.argmax())} | set(np.random.default_rng(1).choice(64, 4).tolist())
+    rows = np.zeros(b.total_q, bool)
+    qsl = b.query_start_loc.numpy()
+    for s in seqs:
+        rows[qsl[s]:qsl[s + 1]] = True
+    compare(b, out, lse, rows=rows)
+
+
+@pytest.mark.parametrize("chunk_last", [False, True])
+def test_hybrid_reduced(chunk_last):
+    b = W.hybrid_chunked(batch=16, chunk=512, history=1500, dec_lo=500, dec_hi=4000, chunk_last=chunk_last)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+def test_hybrid_full_size_sampled():
+    b = W.hybrid_chunked()
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    rows = sample_rows(b.total_q, 48, must=(0, 255, 511, 512, 574))
+    compare(b, out, lse, rows=rows)
+
+
+@pytest.mark.parametrize("mask", [True, False])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("mode", ["tensor", "page_head"])
+def test_fp8_prefill_reduced(mode, layout, mask):
+    b = W.sparse_prefill(kind="e4m3", quant_mode=mode, kv_layout=layout, mask=mask, seq_len=1024)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+def test_bf16_prefill_reduced():
+    for mask in (False, True):
+        b = W.sparse_prefill(kind="bf16", mask=mask, seq_len=1280)
+        g, out, lse, ws = gpu_run(b)
+        compare(b, out, lse)
+
+
+@pytest.mark.parametrize("kind,mode,layout,mask", [("e4m3", "page_head", "HND", True),
+                                                   ("e4m3", "tensor", "NHD", False),
+                                                   ("bf16", None, "NHD", False)])
+def test_prefill_full_size_sampled(kind, mode, layout, mask):
+    b = W.sparse_prefill(kind=kind, quant_mode=mode, kv_layout=layout, mask=mask)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    rows = sample_rows(b.total_q, 40, must=(0, 1, 127, 128, 8191, 8192, 16383))
+    compare(b, out, lse, rows=rows)
+
+
+def test_sliding_window_reduced():
+    b = W.sliding_window(seq_len=2048, window=700)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    # Q = 0 closed form through the kernel: LSE = ln(visible count) with landmarks
+    b.q = torch.zeros_like(b.q)
+    g, out, lse, ws = gpu_run(b)
+    compare(b, out, lse)
+
+
+def test_sliding_window_full_size_sampled(golden):
+    b = W.sliding_window()
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    rows = sample_rows(b.total_q, 40, must=(0, 63, 64, 4095, 4096, 4100, 4159, 8191))
+    compare(b, out, lse, rows=rows)
+
+
+def test_sliding_window_decode_128k():
+    b = W.sliding_window(decode=True)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    h = check_no_device_error(ws, g)
+    # 64 window tiles x 8 kv heads = 512 units: must be split across workers
+    assert h[0] == 512 and h[4] > 0
+    # plain full-context decode over the same 131072 keys
+    b.window, b.landmark_chunk = 0, 0
+    g, out, lse, ws = gpu_run(b)
+    compare(b, out, lse)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def test_page_permutation_bitwise():
+    b = W.splitk_decode(q_len=2, batch=6, ctx_lo=100, ctx_hi=3000)
+    _, o1, l1, _ = gpu_run(b)
+    rng = np.random.default_rng(5)
+    pi = torch.from_numpy(rng.permutation(b.num_pages))
+    k2, v2 = torch.empty_like(b.k_cache), torch.empty_like(b.v_cache)
+    k2[pi], v2[pi] = b.k_cache, b.v_cache
+    bt = b.block_table.clone()
+    m = bt >= 0
+    bt[m] = pi[bt[m].long()].to(torch.int32)
+    b.k_cache, b.v_cache, b.block_table = k2, v2, bt
+    _, o2, l2, _ = gpu_run(b)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_nhd_equals_hnd_bitwise_and_deterministic():
+    a = W.splitk_decode(q_len=4, kv_layout="NHD", batch=6, ctx_lo=100, ctx_hi=3000)
+    c = W.splitk_decode(q_len=4, kv_layout="HND", batch=6, ctx_lo=100, ctx_hi=3000)
+    _, oa, la, _ = gpu_run(a)
+    _, oc, lc, _ = gpu_run(c)
+    assert torch.equal(oa, oc) and torch.equal(la, lc)
+    _, oa2, la2, _ = gpu_run(a)
+    assert torch.equal(oa, oa2) and torch.equal(la, la2)
+    p = W.sparse_prefill(kind="e4m3", quant_mode="page_head", kv_layout="NHD", seq_len=512)
+    p2 = W.sparse_prefill(kind="e4m3", quant_mode="page_head", kv_layout="HND", seq_len=512)
+    _, o1, l1, _ = gpu_run(p)
+    _, o2, l2, _ = gpu_run(p2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forced_split_matches_natural():
+    b = W.hybrid_chunked(batch=8, chunk=300, history=900, dec_lo=200, dec_hi=3000)
+    _, o1, l1, _ = gpu_run(b)
+    P = B.paged_attn_device_info(0)["default_workers"]
+    _, o2, l2, _ = gpu_run(b, force_split_units=1, max_partial_slots=slots_for(b, P, 1))
+    assert (o1.float() - o2.float()).abs().max() <= 2e-2
+    assert (l1 - l2).abs().max() <= 1e-3
+    compare(b, o2, l2)
+
+
+def test_edge_cases():
+    rng = np.random.default_rng(17)
+    # empty q_len sequences, single-key sequences, keys not a multiple of 64, one page per key
+    b = W.build_batch(rng, name="edges", kind="bf16", Hq=8, Hkv=2, d=128, page_size=16,
+                      ctx=[1, 65, 0, 130, 7, 64], q_len=[1, 3, 0, 0, 7, 40], num_pages=40)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    # a window so narrow that landmark-only tiles appear; a row with no visible key
+    b = W.build_batch(rng, name="narrow", kind="bf16", Hq=4, Hkv=1, d=64, page_size=64,
+                      ctx=[300], q_len=[300], window=1, landmark_chunk=2, window_expand_to_chunk=False)
+    g, out, lse, ws = gpu_run(b)
+    O, L = run_oracle(b)
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    empty = ~np.isfinite(L)
+    assert empty.any()
+    assert np.all(l[empty] == -np.inf) and np.all(o[empty] == 0)
+    assert np.abs(o[~empty] - O[~empty]).max() <= 2e-2
+    assert np.abs(l[~empty] - L[~empty]).max() <= 1e-3
+    # non-causal attention
+    b = W.splitk_decode(q_len=3, batch=4, ctx_lo=70, ctx_hi=500)
+    g, out, lse, ws = gpu_run(b, causal=False)
+    compare(b, out, lse, causal=False)
