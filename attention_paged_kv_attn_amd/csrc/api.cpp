@@ -53,7 +53,7 @@ pa_status default_workers(int32_t* out) {
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e);
-  *out = 2 * cus;
+  *out = cus;                  // one persistent workgroup per compute unit
   return PA_OK;
 }
 
@@ -165,7 +165,7 @@ pa_status paged_attn_device_info(int32_t device, pa_device_info* info) {
   std::memset(info, 0, sizeof(*info));
   info->compute_units = prop.multiProcessorCount;
   info->lds_bytes_per_workgroup = static_cast<int32_t>(prop.sharedMemPerBlock);
-  info->default_workers = 2 * prop.multiProcessorCount;
+  info->default_workers = prop.multiProcessorCount;
   std::strncpy(info->arch, prop.gcnArchName, sizeof(info->arch) - 1);
   return PA_OK;
 }

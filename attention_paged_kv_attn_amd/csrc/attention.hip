@@ -57,7 +57,9 @@ struct Cfg {
   static constexpr int V_TILE = 64 * D * (KIND == KIND_F32 ? 4 : 2);  // V staged as bf16 for fp8
   static constexpr int STAGE = K_TILE + V_TILE;
   static constexpr int MERGE = kWaves * kSmallMaxRows * (D + 2) * 4;  // small-path wave merge
-  static constexpr int LDS = (2 * STAGE > MERGE ? 2 * STAGE : MERGE) + kMaskListCap * 2;
+  static constexpr int QOFF = (MERGE + 255) / 256 * 256;               // small-path Q operands
+  static constexpr int QBYTES = KSQ * 64 * (KIND == KIND_F32 ? 4 : KIND == KIND_BF16 ? 16 : 8);
+  static constexpr int LDS = (2 * STAGE > QOFF + QBYTES ? 2 * STAGE : QOFF + QBYTES) + kMaskListCap * 2;
 };
 
 template <int KIND> struct QKOpT;
@@ -119,19 +121,48 @@ __device__ __forceinline__ int page_of(const KParams& p, const SeqCtx& s, int ke
   return page;
 }
 
+// Values the whole wave shares, made explicit for the compiler (so addressing
+// stays in scalar registers and buffer resources need no per-lane loop).
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char* wave_uniform(const char* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Loads at base + soff + voff: `base + soff` is wave-uniform (scalar), voff a
+// 32-bit per-lane offset, so the address is a scalar base plus a VGPR offset
+// when the compiler keeps the base in scalar registers.
+#define PA_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ u32x4 gload16(const char* base, uint32_t voff, uint32_t soff) {
+  return *(const PA_GLOBAL u32x4*)(base + soff + voff);
+}
+__device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_t soff) {
+  return *(const PA_GLOBAL u32x2*)(base + soff + voff);
+}
+__device__ __forceinline__ unsigned gload4(const char* base, uint32_t voff, uint32_t soff) {
+  return *(const PA_GLOBAL unsigned*)(base + soff + voff);
+}
+// Direct HBM -> LDS: every lane fetches 16 B at base + soff + voff; the wave
+// writes them lane-linearly (1 KiB) at the wave-uniform LDS address `dst`.
+__device__ __forceinline__ void gload16_lds(const char* base, char* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_global_load_lds((const PA_GLOBAL void*)(base + soff + voff),
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 // Rows of one 64-key tile.  FAST (page_size >= 64): the tile lies in one page,
 // so the page lookup and the row base are uniform (scalar) and each lane adds a
 // 32-bit offset.  Otherwise every key looks up its own page.
 template <int ELT, bool FAST>
 struct Tile {
-  const char* kb;
+  const char* kb;       // FAST: the tile's first row (key J0, kv head g) in K and V
   const char* vb;
   int J0, nvalid;
   uint32_t kss, vss;   // bytes between consecutive keys of a page
 
   __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s, int tile) {
-    J0 = tile * kUnitKeys;
-    nvalid = min(kUnitKeys, s.ctx - J0);
+    J0 = wave_uniform(tile) * kUnitKeys;
+    nvalid = wave_uniform(min(kUnitKeys, s.ctx - J0));
     kss = (uint32_t)(p.k_ss * ELT);
     vss = (uint32_t)(p.v_ss * ELT);
     if constexpr (FAST) {
@@ -139,6 +170,8 @@ struct Tile {
       const int slot = J0 & (p.page_size - 1);
       kb = reinterpret_cast<const char*>(p.k) + ((int64_t)page * p.k_sp + (int64_t)slot * p.k_ss + (int64_t)s.g * p.k_sh) * ELT;
       vb = reinterpret_cast<const char*>(p.v) + ((int64_t)page * p.v_sp + (int64_t)slot * p.v_ss + (int64_t)s.g * p.v_sh) * ELT;
+      kb = wave_uniform(kb);
+      vb = wave_uniform(vb);
     }
   }
   __device__ __forceinline__ const char* krow(const KParams& p, const SeqCtx& s, int kt) const {
@@ -181,30 +214,40 @@ __device__ __forceinline__ float kscale_of(const KParams& p, const SeqCtx& s, in
   }
 }
 
-// Q / K row -> QK operands of this lane (group h): K-step ks holds dims
-// 32 ks + 8 h .. +7 (bf16, fp8) or 16 (ks / 4) + 4 h + ks % 4 (fp32).
+// QK operands of lane group h from a row: K-step ks holds dims 32 ks + 8 h ..+7
+// (bf16, fp8) or 16 (ks / 4) + 4 h + ks % 4 (fp32).  `at` points at the row's
+// dim 8 h (bf16, fp8) or 4 h (fp32) already; nullptr loads zeros.
+template <int KIND>
+__device__ __forceinline__ int lane_dim_bytes(int h) {
+  return KIND == KIND_F32 ? 16 * h : (KIND == KIND_BF16 ? 16 * h : 8 * h);
+}
+
 template <int KIND, int D>
-__device__ __forceinline__ void load_qk_row(const char* row, int h,
-                                            typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
+__device__ __forceinline__ void load_qk_at(const char* at, typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
   using C = Cfg<KIND, D>;
   if constexpr (KIND == KIND_BF16) {
 #pragma unroll
     for (int ks = 0; ks < C::KSQ; ++ks) {
-      u32x4 v = row ? *reinterpret_cast<const u32x4*>(row + (32 * ks + 8 * h) * 2) : u32x4{0, 0, 0, 0};
+      u32x4 v = at ? *reinterpret_cast<const u32x4*>(at + 64 * ks) : u32x4{0, 0, 0, 0};
       op[ks] = __builtin_bit_cast(bf16x8, v);
     }
   } else if constexpr (KIND == KIND_F8) {
 #pragma unroll
-    for (int ks = 0; ks < C::KSQ; ++ks)
-      op[ks] = row ? *reinterpret_cast<const long*>(row + 32 * ks + 8 * h) : 0L;
+    for (int ks = 0; ks < C::KSQ; ++ks) op[ks] = at ? *reinterpret_cast<const long*>(at + 32 * ks) : 0L;
   } else {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      f32x4 v = row ? *reinterpret_cast<const f32x4*>(row + (16 * c + 4 * h) * 4) : f32x4{0, 0, 0, 0};
+      f32x4 v = at ? *reinterpret_cast<const f32x4*>(at + 64 * c) : f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) op[4 * c + i] = v[i];
     }
   }
+}
+
+template <int KIND, int D>
+__device__ __forceinline__ void load_qk_row(const char* row, int h,
+                                            typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
+  load_qk_at<KIND, D>(row ? row + lane_dim_bytes<KIND>(h) : nullptr, op);
 }
 
 // ---------------------------------------------------------------------------
@@ -216,24 +259,43 @@ struct RowMask {
   bool bit;         // block-mask bit of (row's query tile, the unit's key tile)
 };
 
-__device__ __forceinline__ bool key_visible(const KParams& p, const RowMask& r, int ctx, int key) {
-  bool v = key < ctx;
-  if (p.causal) v = v && key <= r.pos;
-  if (p.window > 0) v = v && key >= r.left;
-  if (p.landmark > 0) v = v && ((key + 1) % p.landmark) != 0;
-  return v && r.bit;
+// Landmark keys (j + 1) % C == 0 inside the tile [J0, J0 + 64) as a bitmap over
+// key offsets; uniform across the workgroup.
+__device__ __forceinline__ uint64_t landmark_bits(const KParams& p, int J0) {
+  uint64_t m = 0;
+  if (p.landmark > 0) {
+    for (int o = p.landmark - 1 - (J0 % p.landmark); o < kUnitKeys; o += p.landmark) m |= 1ull << o;
+  }
+  return m;
 }
 
-// The unit needs no per-element mask for any row of [pos_min, pos_max].
-__device__ __forceinline__ bool unit_is_full(const KParams& p, int J0, int ctx, int pos_min,
-                                             int left_max) {
-  if (J0 + 63 >= ctx) return false;
-  if (p.causal && J0 + 63 > pos_min) return false;
-  if (p.window > 0 && J0 < left_max) return false;
-  if (p.landmark > 0) {
-    const int r0 = p.landmark - 1 - (J0 % p.landmark);     // first landmark offset in the tile
-    if (r0 < 64) return false;
+// Visible key offsets of one row inside a tile: lo <= o < lo + span, minus landmarks.
+struct ElemMask {
+  int lo;
+  unsigned span;
+  uint64_t lm;
+  __device__ __forceinline__ void init(const KParams& p, const RowMask& r, int J0, int nvalid, uint64_t lmk) {
+    int hi = nvalid;
+    if (p.causal) hi = min(hi, r.pos - J0 + 1);
+    lo = p.window > 0 ? max(0, r.left - J0) : 0;
+    span = (r.bit && hi > lo) ? (unsigned)(hi - lo) : 0u;
+    lm = lmk;
   }
+  __device__ __forceinline__ bool ok(int o) const {
+    bool v = (unsigned)(o - lo) < span;
+    if (lm) v = v && !((lm >> o) & 1ull);
+    return v;
+  }
+};
+
+// The tile needs no per-element mask for any row with positions in [pos_min, ...]
+// and window starts <= left_max.
+__device__ __forceinline__ bool unit_is_full(const KParams& p, int J0, int nvalid, int pos_min,
+                                             int left_max, uint64_t lmk) {
+  if (nvalid < kUnitKeys) return false;
+  if (p.causal && J0 + kUnitKeys - 1 > pos_min) return false;
+  if (p.window > 0 && J0 < left_max) return false;
+  if (lmk) return false;
   if (p.bm) return false;
   return true;
 }
@@ -344,18 +406,38 @@ __device__ __forceinline__ void v_words(const typename VRawT<KIND, MD>::T& r, un
 // normalised partial (fp32) and its LSE into a slot.  `o` holds the lane's
 // MD x 4 values in accumulator order.
 // ---------------------------------------------------------------------------
-template <int KIND, int D>
+// Head dim held by accumulator element j of O^T M-block md in lane group h.
+// TRV: V^T operands read by transpose loads from a row-major V tile (dims 16 md + m).
+template <int KIND, int D, bool TRV = false>
 __device__ __forceinline__ int out_dim(int h, int j, int md) {
-  if constexpr (KIND == KIND_F32) return 4 * (4 * h + j) + (md & 3) + 64 * (md >> 2);
+  if constexpr (TRV) return 16 * md + 4 * h + j;
+  else if constexpr (KIND == KIND_F32) return 4 * (4 * h + j) + (md & 3) + 64 * (md >> 2);
   else return Cfg<KIND, D>::MD * (4 * h + j) + md;
 }
 
-template <int KIND, int D>
+template <int KIND, int D, bool TRV = false>
 __device__ __forceinline__ void write_row(const KParams& p, const QBlock& x, int r, int h,
                                           const f32x4 (&acc)[Cfg<KIND, D>::MD], float inv_l,
                                           float lse, bool final_out, int slot) {
   constexpr int MD = Cfg<KIND, D>::MD;
   const int tok = x.q0 + x.t0 + r / p.G, head = x.g * p.G + r % p.G;
+  if constexpr (TRV) {
+    if (final_out) {
+      char* o = reinterpret_cast<char*>(p.out) + (tok * p.o_st + head * p.o_sh) * 2;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        *reinterpret_cast<u32x2*>(o + out_dim<KIND, D, true>(h, 0, md) * 2) =
+            u32x2{pack_bf16x2(acc[md][0] * inv_l, acc[md][1] * inv_l), pack_bf16x2(acc[md][2] * inv_l, acc[md][3] * inv_l)};
+      if (h == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
+    } else {
+      float* o = p.part_o + ((int64_t)slot * kLargeRows + r) * D;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        *reinterpret_cast<f32x4*>(o + out_dim<KIND, D, true>(h, 0, md)) = acc[md] * inv_l;
+      if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+    }
+    return;
+  }
   if (final_out) {
     if constexpr (KIND == KIND_F32) {
       float* o = reinterpret_cast<float*>(p.out) + tok * p.o_st + head * p.o_sh;
@@ -415,10 +497,13 @@ __device__ void build_tile_list(const KParams& p, const QBlock& x, int t_lo, int
 
 // ---------------------------------------------------------------------------
 // small Q-blocks (<= 16 rows): one wave runs a contiguous run of units with
-// operands loaded straight from HBM into registers, as a rolling pipeline:
-// the K loads of tile u+1 are issued as soon as S(u) has consumed K(u), and
-// its V loads as soon as PV(u) has consumed V(u), so every wave always has
-// about one tile of loads in flight.
+// operands loaded straight from HBM into registers.  Each wave keeps exactly
+// one tile (32 KiB of K and V) in flight: issue the tile's loads, consume
+// them, then issue the next tile.  Measured on MI355X with this access
+// pattern, one tile in flight per wave sustains ~6.2 TB/s while also
+// prefetching the next tile during compute drops to ~3.7 TB/s (the extra
+// outstanding requests congest the memory system); only the next tile's page
+// number is fetched ahead (a scalar load).
 // ---------------------------------------------------------------------------
 template <int KIND, int D>
 struct SmallRegs {
@@ -432,106 +517,243 @@ struct SmallRegs {
   f32x4 vf[KIND == KIND_F32 ? 4 : 1][KIND == KIND_F32 ? 4 : 1][KIND == KIND_F32 ? D / 64 : 1];
 };
 
+// QK operands from a buffer: K-step ks of lane group h at voff + (ks part), soff.
+template <int KIND, int D>
+__device__ __forceinline__ void bload_qk(const char* r, uint32_t voff, uint32_t soff,
+                                         typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
+  using C = Cfg<KIND, D>;
+  if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks) op[ks] = __builtin_bit_cast(bf16x8, gload16(r, voff + 64 * ks, soff));
+  } else if constexpr (KIND == KIND_F8) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks) op[ks] = __builtin_bit_cast(long, gload8(r, voff + 32 * ks, soff));
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const f32x4 v = __builtin_bit_cast(f32x4, gload16(r, voff + 64 * c, soff));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) op[4 * c + i] = v[i];
+    }
+  }
+}
+
+template <int KIND, int MD>
+__device__ __forceinline__ typename VRawT<KIND, MD>::T bload_v(const char* r, uint32_t voff, uint32_t soff) {
+  using T = typename VRawT<KIND, MD>::T;
+  if constexpr (sizeof(T) == 16) return gload16(r, voff, soff);
+  else if constexpr (sizeof(T) == 8) return gload8(r, voff, soff);
+  else return gload4(r, voff, soff);
+}
+
 template <int KIND, int D, bool FAST>
 __device__ __forceinline__ void small_load_k(const KParams& p, const SeqCtx& s, const Tile<Cfg<KIND, D>::ELT, FAST>& t,
                                              SmallRegs<KIND, D>& r, int n, int h) {
+  if constexpr (FAST) {
+    if (t.nvalid == kUnitKeys) {
+      const uint32_t lane = (uint32_t)n * t.kss + lane_dim_bytes<KIND>(h);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) load_qk_row<KIND, D>(t.krow(p, s, 16 * mb + n), h, r.kA[mb]);
+      for (int mb = 0; mb < 4; ++mb) bload_qk<KIND, D>(t.kb, lane, 16 * mb * t.kss, r.kA[mb]);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        bload_qk<KIND, D>(t.kb, (uint32_t)min(16 * mb + n, t.nvalid - 1) * t.kss + lane_dim_bytes<KIND>(h), 0u,
+                          r.kA[mb]);
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) load_qk_row<KIND, D>(t.krow(p, s, 16 * mb + n), h, r.kA[mb]);
+  }
 }
 
 template <int KIND, int D, bool FAST>
 __device__ __forceinline__ void small_load_v(const KParams& p, const SeqCtx& s, const Tile<Cfg<KIND, D>::ELT, FAST>& t,
                                              SmallRegs<KIND, D>& r, int n, int h) {
   constexpr int MD = Cfg<KIND, D>::MD;
+  constexpr int ELT = Cfg<KIND, D>::ELT;
+  if constexpr (KIND == KIND_F32) {
+    // rows 16 mb + 4 h + j, dims 64 gd + 4 n
+    if constexpr (FAST) {
+      const bool full = t.nvalid == kUnitKeys;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kt = 16 * mb + 4 * h + j;
+          const uint32_t voff = full ? (uint32_t)(4 * h) * t.vss + 16 * n
+                                     : (uint32_t)min(kt, t.nvalid - 1) * t.vss + 16 * n;
+          const uint32_t soff = full ? (uint32_t)(16 * mb + j) * t.vss : 0u;
+#pragma unroll
+          for (int gd = 0; gd < D / 64; ++gd)
+            r.vf[mb][j][gd] = __builtin_bit_cast(f32x4, gload16(t.vb, voff + 256 * gd, soff));
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const char* row = t.vrow(p, s, 16 * mb + 4 * h + j) + 16 * n;
+#pragma unroll
+          for (int gd = 0; gd < D / 64; ++gd) r.vf[mb][j][gd] = *reinterpret_cast<const f32x4*>(row + 256 * gd);
+        }
+    }
+  } else {
+    // piece (ks2, pc): row 32 ks2 + 16 (pc / 4) + 4 h + pc % 4, dims MD n ..
+    if constexpr (FAST) {
+      if (t.nvalid == kUnitKeys) {
+        const uint32_t lane = (uint32_t)(4 * h) * t.vss + MD * n * ELT;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int pc = 0; pc < 8; ++pc)
+            r.vr[ks2][pc] = bload_v<KIND, MD>(t.vb, lane, (32 * ks2 + 16 * (pc >> 2) + (pc & 3)) * t.vss);
+      } else {
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int pc = 0; pc < 8; ++pc) {
+            const int kt = min(32 * ks2 + 16 * (pc >> 2) + 4 * h + (pc & 3), t.nvalid - 1);
+            r.vr[ks2][pc] = bload_v<KIND, MD>(t.vb, (uint32_t)kt * t.vss + MD * n * ELT, 0u);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc)
+          r.vr[ks2][pc] = load_v_raw<KIND, MD>(t.vrow(p, s, 32 * ks2 + 16 * (pc >> 2) + 4 * h + (pc & 3)), MD * n);
+    }
+  }
+}
+
+// Apply the per-element mask of one row-block (lane's row) to log2-domain scores.
+__device__ __forceinline__ void mask_scores(f32x4 (&sc)[4], const ElemMask& em, int h) {
+  if (em.lm) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = 16 * mb + 4 * h + j;
+        const bool ok = ((unsigned)(o - em.lo) < em.span) && !((em.lm >> o) & 1ull);
+        sc[mb][j] = ok ? sc[mb][j] : kNegInf;
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = 16 * mb + 4 * h + j;
+        sc[mb][j] = ((unsigned)(o - em.lo) < em.span) ? sc[mb][j] : kNegInf;
+      }
+  }
+}
+
+// Q operands of a small Q-block, either staged in LDS (shared by the four
+// waves of one segment) or held in registers (one wave streaming Q-blocks).
+template <int KIND, int D>
+struct QFromLds {
+  const typename QKOpT<KIND>::T* q;
+  __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int lane) const { return q[ks * 64 + lane]; }
+};
+template <int KIND, int D>
+struct QFromRegs {
+  const typename QKOpT<KIND>::T* q;   // the wave's own operands, indexed by K-step
+  __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int) const { return q[ks]; }
+};
+
+template <int KIND, int D, bool FAST, class QSrc>
+__device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s, const QBlock& x,
+                                              const Tile<Cfg<KIND, D>::ELT, FAST>& tc, const SmallRegs<KIND, D>& r,
+                                              const QSrc& qsrc, RowMask& rm, int bm_head,
+                                              int pos_min, int left_max, WaveState<KIND, D, 1>& st, int lane) {
+  using C = Cfg<KIND, D>;
+  constexpr int MD = C::MD;
+  const int h = lane >> 4;
+  const int J0 = tc.J0;
+  float vsc;
+  const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
+  if (p.bm) {
+    const int kt = J0 / p.bm_tile, qt = rm.pos / p.bm_tile;
+    rm.bit = kt < p.bm_nk && qt < p.bm_nq &&
+             p.bm[x.b * p.bm_sb + bm_head * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+  }
+  // S^T = K Q^T (Q operands re-read from LDS)
+  f32x4 sc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) sc[mb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < C::KSQ; ++ks) {
+    const typename QKOpT<KIND>::T qb = qsrc(ks, lane);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) sc[mb] = mfma_qk(r.kA[mb][ks], qb, sc[mb]);
+  }
+  const uint64_t lmk = landmark_bits(p, J0);
+  const bool full = unit_is_full(p, J0, tc.nvalid, pos_min, left_max, lmk);
+  float cs = p.sm_log2;
+  if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) sc[mb] *= cs;
+  if (!full) {
+    ElemMask em;
+    em.init(p, rm, J0, tc.nvalid, lmk);
+    mask_scores(sc, em, h);
+  }
+  softmax_update<KIND, D, 1>(st, 0, sc);
+  // O^T += V^T P^T
   if constexpr (KIND == KIND_F32) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const char* row = t.vrow(p, s, 16 * mb + 4 * h + j);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int gd = 0; gd < D / 64; ++gd) r.vf[mb][j][gd] = *reinterpret_cast<const f32x4*>(row + (64 * gd + 4 * n) * 4);
-      }
+        for (int md = 0; md < MD; ++md)
+          st.acc[0][md] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.vf[mb][j][md >> 2][md & 3], sc[mb][j],
+                                                                st.acc[0][md], 0, 0, 0);
   } else {
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      unsigned w[8][MD / 2];
 #pragma unroll
-      for (int pc = 0; pc < 8; ++pc)
-        r.vr[ks2][pc] = load_v_raw<KIND, MD>(t.vrow(p, s, 32 * ks2 + 16 * (pc >> 2) + 4 * h + (pc & 3)), MD * n);
+      for (int pc = 0; pc < 8; ++pc) v_words<KIND, MD>(r.vr[ks2][pc], w[pc]);
+      const bf16x8 pb = p_operand(sc, ks2, vsc);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) st.acc[0][md] = mfma_pv(v_operand<MD>(w, md), pb, st.acc[0][md]);
+    }
   }
 }
 
+// Double-buffered: the K/V loads of tile u + 1 are in flight while tile u is
+// computed (two static register sets, the loop unrolled by two).
 template <int KIND, int D, bool FAST>
 __device__ __forceinline__ void small_run(const KParams& p, const SeqCtx& s, const QBlock& x, const short* list,
                                           int c0, int t_lo, int a, int b,
-                                          const typename QKOpT<KIND>::T (&qB)[Cfg<KIND, D>::KSQ], RowMask rm,
+                                          const typename QKOpT<KIND>::T* qlds, RowMask rm,
                                           int bm_head, int pos_min, int left_max, WaveState<KIND, D, 1>& st,
                                           int lane) {
   using C = Cfg<KIND, D>;
-  constexpr int MD = C::MD;
   const int n = lane & 15, h = lane >> 4;
-  auto tile_of = [&](int u) { return p.bm ? (int)list[u - c0] : t_lo + u; };
-  Tile<C::ELT, FAST> tc;
-  tc.init(p, s, tile_of(a));
-  SmallRegs<KIND, D> r;
-  small_load_k<KIND, D, FAST>(p, s, tc, r, n, h);
-  small_load_v<KIND, D, FAST>(p, s, tc, r, n, h);
-  for (int u = a; u < b; ++u) {
-    const bool more = u + 1 < b;
-    Tile<C::ELT, FAST> tn = tc;
-    if (more) tn.init(p, s, tile_of(u + 1));
-    const int J0 = tc.J0;
-    float vsc;
-    const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
-    if (p.bm) {
-      const int kt = J0 / p.bm_tile, qt = rm.pos / p.bm_tile;
-      rm.bit = kt < p.bm_nk && qt < p.bm_nq &&
-               p.bm[x.b * p.bm_sb + bm_head * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+  auto tile_of = [&](int u) {   // wave-uniform: keeps tile addressing in scalar registers
+    return __builtin_amdgcn_readfirstlane(p.bm ? (int)list[u - c0] : t_lo + u);
+  };
+  Tile<C::ELT, FAST> ta, tb;
+  SmallRegs<KIND, D> ra, rb;
+  ta.init(p, s, tile_of(a));
+  small_load_k<KIND, D, FAST>(p, s, ta, ra, n, h);
+  small_load_v<KIND, D, FAST>(p, s, ta, ra, n, h);
+  for (int u = a; u < b; u += 2) {
+    if (u + 1 < b) {
+      tb.init(p, s, tile_of(u + 1));
+      small_load_k<KIND, D, FAST>(p, s, tb, rb, n, h);
+      small_load_v<KIND, D, FAST>(p, s, tb, rb, n, h);
     }
-    // S^T = K Q^T
-    f32x4 sc[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      sc[mb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < C::KSQ; ++ks) sc[mb] = mfma_qk(r.kA[mb][ks], qB[ks], sc[mb]);
+    small_compute<KIND, D, FAST>(p, s, x, ta, ra, QFromLds<KIND, D>{qlds}, rm, bm_head, pos_min, left_max, st, lane);
+    if (u + 1 >= b) break;
+    if (u + 2 < b) {
+      ta.init(p, s, tile_of(u + 2));
+      small_load_k<KIND, D, FAST>(p, s, ta, ra, n, h);
+      small_load_v<KIND, D, FAST>(p, s, ta, ra, n, h);
     }
-    if (more) small_load_k<KIND, D, FAST>(p, s, tn, r, n, h);
-    const bool full = unit_is_full(p, J0, s.ctx, pos_min, left_max);
-    float cs = p.sm_log2;
-    if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v = sc[mb][j] * cs;
-        if (!full && !key_visible(p, rm, s.ctx, J0 + 16 * mb + 4 * h + j)) v = kNegInf;
-        sc[mb][j] = v;
-      }
-    softmax_update<KIND, D, 1>(st, 0, sc);
-    // O^T += V^T P^T
-    if constexpr (KIND == KIND_F32) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int md = 0; md < MD; ++md)
-            st.acc[0][md] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.vf[mb][j][md >> 2][md & 3], sc[mb][j],
-                                                                  st.acc[0][md], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        unsigned w[8][MD / 2];
-#pragma unroll
-        for (int pc = 0; pc < 8; ++pc) v_words<KIND, MD>(r.vr[ks2][pc], w[pc]);
-        const bf16x8 pb = p_operand(sc, ks2, vsc);
-#pragma unroll
-        for (int md = 0; md < MD; ++md) st.acc[0][md] = mfma_pv(v_operand<MD>(w, md), pb, st.acc[0][md]);
-      }
-    }
-    if (more) small_load_v<KIND, D, FAST>(p, s, tn, r, n, h);
-    tc = tn;
+    small_compute<KIND, D, FAST>(p, s, x, tb, rb, QFromLds<KIND, D>{qlds}, rm, bm_head, pos_min, left_max, st, lane);
   }
 }
 
@@ -549,9 +771,17 @@ __device__ void small_segment(const KParams& p, const QBlock& x, int t_lo, int t
   const bool row_ok = n < x.rows;
   const int r = row_ok ? n : 0;
   const int tok = x.q0 + x.t0 + r / p.G, head = x.g * p.G + r % p.G;
-  typename QKOpT<KIND>::T qB[C::KSQ];
-  load_qk_row<KIND, D>(row_ok ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
-                              : nullptr, h, qB);
+  // Q operands of the 16 rows, in operand order [ks][lane], after the merge area
+  using QT = typename QKOpT<KIND>::T;
+  QT* qlds = reinterpret_cast<QT*>(smem + C::QOFF);
+  if (wave == 0) {
+    QT qB[C::KSQ];
+    load_qk_row<KIND, D>(row_ok ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
+                                : nullptr, h, qB);
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks) qlds[ks * 64 + lane] = qB[ks];
+  }
+  __syncthreads();
   RowMask rm;
   rm.pos = x.ctx - x.ql + x.t0 + r / p.G;
   rm.left = p.window > 0 ? window_left(p, rm.pos) : 0;
@@ -568,7 +798,7 @@ __device__ void small_segment(const KParams& p, const QBlock& x, int t_lo, int t
     const int cn = min(kMaskListCap, u1 - c0);
     if (p.bm) build_tile_list(p, x, t_lo, t_hi, c0, cn, list);
     const int a = c0 + (cn * wave) / kWaves, b = c0 + (cn * (wave + 1)) / kWaves;
-    if (a < b) small_run<KIND, D, FAST>(p, s, x, list, c0, t_lo, a, b, qB, rm, bm_head, pos_min, left_max, st, lane);
+    if (a < b) small_run<KIND, D, FAST>(p, s, x, list, c0, t_lo, a, b, qlds, rm, bm_head, pos_min, left_max, st, lane);
     if (p.bm) __syncthreads();                 // list reuse
   }
 
@@ -648,44 +878,64 @@ struct Stage {
   u32x4 vf[KIND == KIND_F32 ? VCH : 1];
   typename VRawT<KIND == KIND_F32 ? KIND_BF16 : KIND, MD>::T vraw[KIND == KIND_F32 ? 1 : 4];
 
-  // global -> registers for the given tile
+  // global -> registers for the given tile.  Thread t stages K chunks
+  // c = i * 256 + t (lane c % 64 of operand (mb, ks) = c / 64, a row of the
+  // tile: key 16 mb + lane % 16) and V rows 32 ks2 + 16 half + 4 (lane / 16) + j.
   __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile) {
     Tile<C::ELT, FAST> t;
     t.init(p, s, tile);
     const int tid = threadIdx.x;
+    const int ln = tid & 63, m = ln & 15, hh = ln >> 4;
+    const bool full = t.nvalid == kUnitKeys;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = i * kThreads + tid;
-      const int ln = c & 63, mk = c >> 6;
-      const int m = ln & 15, hh = ln >> 4;
+      const int mk = (i * kThreads + tid) >> 6;            // uniform per wave
+      int mb, col;                                          // col: byte offset in the row
       if constexpr (KIND == KIND_F32) {
-        const int mb = mk / (D / 16), cc = mk % (D / 16);
-        kr[i] = *reinterpret_cast<const u32x4*>(t.krow(p, s, 16 * mb + m) + (16 * cc + 4 * hh) * 4);
+        mb = mk / (D / 16);
+        col = (16 * (mk % (D / 16)) + 4 * hh) * 4;
       } else {
-        const int mb = mk / C::KSQ, ks = mk % C::KSQ;
-        const char* row = t.krow(p, s, 16 * mb + m);
-        if constexpr (KIND == KIND_BF16) kr[i] = *reinterpret_cast<const u32x4*>(row + (32 * ks + 8 * hh) * 2);
-        else kr[i] = *reinterpret_cast<const u32x2*>(row + 32 * ks + 8 * hh);
+        mb = mk / C::KSQ;
+        col = (32 * (mk % C::KSQ) + 8 * hh) * C::ELT;
       }
+      const char* row;
+      if constexpr (FAST) {
+        row = full ? t.kb + 16 * mb * t.kss + ((uint32_t)m * t.kss + col)
+                   : t.kb + ((uint32_t)min(16 * mb + m, t.nvalid - 1) * t.kss + col);
+      } else {
+        row = t.krow(p, s, 16 * mb + m) + col;
+      }
+      kr[i] = *reinterpret_cast<const KReg*>(row);
     }
     if constexpr (KIND == KIND_F32) {
 #pragma unroll
       for (int i = 0; i < VCH; ++i) {
-        const int c = i * kThreads + tid;
-        const int ln = c & 63, grp = c >> 6;            // grp = (mb * 4 + j) * (D / 64) + gd
+        const int grp = (i * kThreads + tid) >> 6;           // (mb * 4 + j) * (D / 64) + gd, uniform per wave
         const int gd = grp % (D / 64), mbj = grp / (D / 64);
         const int mb = mbj >> 2, j = mbj & 3;
-        const int m = ln & 15, hh = ln >> 4;
-        vf[i] = *reinterpret_cast<const u32x4*>(t.vrow(p, s, 16 * mb + 4 * hh + j) + (64 * gd + 4 * m) * 4);
+        const int kt = 16 * mb + 4 * hh + j;
+        const char* row;
+        if constexpr (FAST) row = t.vb + (uint32_t)(full ? kt : min(kt, t.nvalid - 1)) * t.vss;
+        else row = t.vrow(p, s, kt);
+        vf[i] = *reinterpret_cast<const u32x4*>(row + (64 * gd + 4 * m) * 4);
       }
     } else {
       // thread -> (ks2, lane_t, half); 4 rows j = 0..3
       const int task = tid >> 1, half = tid & 1;
-      const int ks2 = task >> 6, ln = task & 63;
-      const int m = ln & 15, hh = ln >> 4;
+      const int ks2 = task >> 6, lt = task & 63;
+      const int mm = lt & 15, h2 = lt >> 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vraw[j] = load_v_raw<KIND, MD>(t.vrow(p, s, 32 * ks2 + 16 * half + 4 * hh + j), MD * m);
+      for (int j = 0; j < 4; ++j) {
+        const int kt = 32 * ks2 + 16 * half + 4 * h2 + j;
+        const char* row;
+        if constexpr (FAST) {
+          row = full ? t.vb + (32 * ks2 + j) * t.vss + ((uint32_t)(16 * half + 4 * h2) * t.vss + MD * mm * C::ELT)
+                     : t.vb + ((uint32_t)min(kt, t.nvalid - 1) * t.vss + MD * mm * C::ELT);
+          vraw[j] = load_v_raw<KIND, MD>(row, 0);
+        } else {
+          vraw[j] = load_v_raw<KIND, MD>(t.vrow(p, s, kt), MD * mm);
+        }
+      }
     }
   }
 
@@ -726,16 +976,72 @@ struct Stage {
   }
 };
 
+// bf16, d = 128, one page per tile: K and V go straight from HBM into LDS
+// (buffer_load ... lds), no staging registers.  K operand (mb, ks) = mk lands
+// lane-linearly at kbuf + 1 KiB * mk, which is MFMA operand order.  V rows
+// 4 r4 .. 4 r4 + 3 land at vbuf + 1 KiB * r4, row-major with row r's 16-byte
+// chunk q stored in slot q ^ 2 (r % 8), so the transpose reads of a V^T
+// operand (16 rows x 32 bytes) spread over all LDS banks.
+struct DirectStage {
+  __device__ __forceinline__ static void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
+    Tile<2, true> t;
+    t.init(p, s, tile);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m = lane & 15, hh = lane >> 4;
+    const bool full = t.nvalid == kUnitKeys;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mk = 4 * i + wave, mb = mk >> 2, ks = mk & 3;
+      const uint32_t voff = full ? (uint32_t)m * t.kss + 16 * hh
+                                 : (uint32_t)min(16 * mb + m, t.nvalid - 1) * t.kss + 16 * hh;
+      const uint32_t soff = full ? (uint32_t)(16 * mb) * t.kss + 64 * ks : 64u * ks;
+      gload16_lds(t.kb, kbuf + 1024 * mk, voff, soff);
+    }
+    const int sl = lane & 15, rl = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r4 = 4 * i + wave, row = 4 * r4 + rl;
+      const int q = sl ^ (2 * (row & 7));
+      const uint32_t voff = full ? (uint32_t)rl * t.vss + 16 * q
+                                 : (uint32_t)min(row, t.nvalid - 1) * t.vss + 16 * q;
+      const uint32_t soff = full ? (uint32_t)(4 * r4) * t.vss : 0u;
+      gload16_lds(t.vb, vbuf + 1024 * r4, voff, soff);
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// V^T operand (ks2, md) of a row-major swizzled V tile by two transpose reads:
+// in each 16-lane group h, lane i = 4 k + c points at row 32 ks2 + 4 h + k
+// (+16 for slots 4..7), dims 16 md + 4 c; the read hands lane i the dim
+// 16 md + i of those 4 rows.  `base0` is the lane's byte offset with md = 0
+// (row part + swizzle bits), so the md offset is an XOR on bits 5..7.
+__device__ __forceinline__ bf16x8 v_operand_tr(const char* smem, uint32_t base0, int ks2, int md) {
+  const uint32_t a = (base0 + ks2 * 8192u) ^ (32u * md);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(smem + a));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(smem + a + 4096));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
 template <int KIND, int D, bool FAST>
 __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t_hi, int u0, int u1,
                               bool final_out, int slot, char* smem) {
   using C = Cfg<KIND, D>;
   constexpr int MD = C::MD;
   constexpr int NB = 2;
+  constexpr bool DIRECT = KIND == KIND_BF16 && D == 128 && FAST;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, h = lane >> 4;
   short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
   SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
+  // transpose-read lane offset (see v_operand_tr), relative to a V buffer
+  const int trk = n >> 2, trc = n & 3;
+  const uint32_t tr_lane = (uint32_t)(4 * h + trk) * 256u + 32u * ((4 * h + trk) & 7) + 16u * (trc >> 1) + 8u * (trc & 1);
 
   // this lane's two rows
   typename QKOpT<KIND>::T qB[NB][C::KSQ];
@@ -773,16 +1079,31 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
     const int cn = min(kMaskListCap, u1 - c0);
     if (p.bm) build_tile_list(p, x, t_lo, t_hi, c0, cn, list);
-    auto tile_of = [&](int u) { return p.bm ? (int)list[u - c0] : t_lo + u; };
-    stg.load(p, s, tile_of(c0));
-    stg.store(smem, smem + C::K_TILE);
+    auto tile_of = [&](int u) {   // wave-uniform: keeps tile addressing in scalar registers
+    return __builtin_amdgcn_readfirstlane(p.bm ? (int)list[u - c0] : t_lo + u);
+  };
+    if constexpr (DIRECT) {
+      DirectStage::load(p, s, tile_of(c0), smem, smem + C::K_TILE);
+      wait_vmem();
+    } else {
+      stg.load(p, s, tile_of(c0));
+      stg.store(smem, smem + C::K_TILE);
+    }
     __syncthreads();
     for (int u = c0; u < c0 + cn; ++u) {
       const int buf = (u - c0) & 1;
       char* kbuf = smem + buf * C::STAGE;
       char* vbuf = kbuf + C::K_TILE;
       const bool more = u + 1 < c0 + cn;
-      if (more) stg.load(p, s, tile_of(u + 1));
+      if (more) {
+        if constexpr (DIRECT) {
+          char* nk = smem + (buf ^ 1) * C::STAGE;
+          DirectStage::load(p, s, tile_of(u + 1), nk, nk + C::K_TILE);
+        } else {
+          stg.load(p, s, tile_of(u + 1));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       const int tile = tile_of(u);
       const int J0 = tile * kUnitKeys;
       if (wave_live) {
@@ -798,7 +1119,9 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
                          p.bm[x.b * p.bm_sb + bm_head[nb] * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
           }
         }
-        const bool full = unit_is_full(p, J0, x.ctx, pos_min, left_max);
+        const int nvalid = min(kUnitKeys, x.ctx - J0);
+        const uint64_t lmk = landmark_bits(p, J0);
+        const bool full = unit_is_full(p, J0, nvalid, pos_min, left_max, lmk);
         // S^T = K Q^T
         f32x4 sc[NB][4];
 #pragma unroll
@@ -833,13 +1156,12 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float v = sc[nb][mb][j] * cs;
-              if (!full && !key_visible(p, rm[nb], x.ctx, J0 + 16 * mb + 4 * h + j)) v = kNegInf;
-              sc[nb][mb][j] = v;
-            }
+          for (int mb = 0; mb < 4; ++mb) sc[nb][mb] *= cs;
+          if (!full) {
+            ElemMask em;
+            em.init(p, rm[nb], J0, nvalid, lmk);
+            mask_scores(sc[nb], em, h);
+          }
           softmax_update<KIND, D, NB>(st, nb, sc[nb]);
         }
         // O^T += V^T P^T
@@ -857,6 +1179,20 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
                   for (int nb = 0; nb < NB; ++nb)
                     st.acc[nb][4 * gd + i] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], sc[nb][mb][j], st.acc[nb][4 * gd + i], 0, 0, 0);
               }
+        } else if constexpr (DIRECT) {
+          const uint32_t base0 = (uint32_t)(vbuf - smem) + tr_lane;
+#pragma unroll
+          for (int ks2 = 0; ks2 < 2; ++ks2) {
+            bf16x8 pb[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) pb[nb] = p_operand(sc[nb], ks2, vsc);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+              const bf16x8 va = v_operand_tr(smem, base0, ks2, md);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) st.acc[nb][md] = mfma_pv(va, pb[nb], st.acc[nb][md]);
+            }
+          }
         } else {
 #pragma unroll
           for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -872,7 +1208,10 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
           }
         }
       }
-      if (more) {
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DIRECT) {
+        if (more) wait_vmem();
+      } else if (more) {
         char* nk = smem + (buf ^ 1) * C::STAGE;
         stg.store(nk, nk + C::K_TILE);
       }
@@ -890,7 +1229,7 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
     const float lse = empty ? kNegInf : (st.m2[nb] + log2f(l)) * kLn2;
-    write_row<KIND, D>(p, x, rowi[nb], h, st.acc[nb], inv, lse, final_out, slot);
+    write_row<KIND, D, DIRECT>(p, x, rowi[nb], h, st.acc[nb], inv, lse, final_out, slot);
   }
 }
 
@@ -898,7 +1237,7 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
 // the persistent kernel
 // ---------------------------------------------------------------------------
 template <int KIND, int D, bool FAST>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 1) void attention_kernel(KParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int U = p.hdr[H_U];
   const int L = p.hdr[H_L];

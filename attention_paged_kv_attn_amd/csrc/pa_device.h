@@ -105,11 +105,15 @@ struct QBlock {
 __device__ __forceinline__ QBlock load_qblock(const KParams& p, int q) {
   QBlock x;
   const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[q];
-  x.b = d.x; x.g = d.y; x.t0 = d.z; x.nt = d.w;
+  // every lane of the wave reads the same descriptor: keep it in scalar registers
+  x.b = __builtin_amdgcn_readfirstlane(d.x);
+  x.g = __builtin_amdgcn_readfirstlane(d.y);
+  x.t0 = __builtin_amdgcn_readfirstlane(d.z);
+  x.nt = __builtin_amdgcn_readfirstlane(d.w);
   x.rows = x.nt * p.G;
-  x.q0 = p.qsl[x.b];
-  x.ql = p.qsl[x.b + 1] - x.q0;
-  x.ctx = p.seq_lens[x.b];
+  x.q0 = __builtin_amdgcn_readfirstlane(p.qsl[x.b]);
+  x.ql = __builtin_amdgcn_readfirstlane(p.qsl[x.b + 1]) - x.q0;
+  x.ctx = __builtin_amdgcn_readfirstlane(p.seq_lens[x.b]);
   x.pos_lo = x.ctx - x.ql + x.t0;
   x.pos_hi = x.pos_lo + x.nt - 1;
   return x;

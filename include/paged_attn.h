@@ -109,7 +109,7 @@ typedef struct pa_params {
   int32_t landmark_chunk;       /* C > 0: hide keys with (j + 1) % C == 0 */
   int32_t block_mask_tile;      /* tile edge of block_mask in tokens; multiple of 64; 0 = 128 */
   /* scheduling */
-  int32_t num_workers;          /* P persistent workgroups; 0 = 2 per compute unit */
+  int32_t num_workers;          /* P persistent workgroups; 0 = one per compute unit */
   int32_t split_min_units;      /* L_min: fewest 64-key units a worker is given; 0 = 8 */
   int32_t force_split_units;    /* > 0: every worker gets exactly this many units (testing) */
   int32_t max_partial_slots;    /* capacity for split partial outputs; 0 = 2 * P */
