@@ -59,7 +59,14 @@ struct Cfg {
   static constexpr int MERGE = kWaves * kSmallMaxRows * (D + 2) * 4;  // small-path wave merge
   static constexpr int QOFF = (MERGE + 255) / 256 * 256;               // small-path Q operands
   static constexpr int QBYTES = KSQ * 64 * (KIND == KIND_F32 ? 4 : KIND == KIND_BF16 ? 16 : 8);
-  static constexpr int LDS = (2 * STAGE > QOFF + QBYTES ? 2 * STAGE : QOFF + QBYTES) + kMaskListCap * 2;
+  // small_range: merge stash of 8 cut pieces, then two Q-operand slots per wave
+  static constexpr int STASH = (2 * kWaves) * (32 + 16 * D) * 4 + 2 * kWaves * 4;
+  static constexpr int QSLOT = 64 * KSQ * (KIND == KIND_F32 ? 4 : KIND == KIND_BF16 ? 16 : 8);
+  static constexpr int QSLOTS_OFF = (STASH + 255) / 256 * 256;
+  static constexpr int STREAM = QSLOTS_OFF + 2 * kWaves * QSLOT;
+  static constexpr int BODY0 = 2 * STAGE > QOFF + QBYTES ? 2 * STAGE : QOFF + QBYTES;
+  static constexpr int LDS = (BODY0 > STREAM ? BODY0 : STREAM) + kMaskListCap * 2;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 template <int KIND> struct QKOpT;
@@ -158,15 +165,29 @@ struct Tile {
   const char* kb;       // FAST: the tile's first row (key J0, kv head g) in K and V
   const char* vb;
   int J0, nvalid;
+  int page;             // FAST: physical page of the tile
   uint32_t kss, vss;   // bytes between consecutive keys of a page
 
+  // FAST only: the page holding key J0 is already known
+  __device__ __forceinline__ void init_at_page(const KParams& p, const SeqCtx& s, int tile, int page) {
+    J0 = wave_uniform(tile) * kUnitKeys;
+    nvalid = wave_uniform(min(kUnitKeys, s.ctx - J0));
+    kss = (uint32_t)(p.k_ss * ELT);
+    vss = (uint32_t)(p.v_ss * ELT);
+    this->page = page;
+    const int slot = J0 & (p.page_size - 1);
+    kb = wave_uniform(reinterpret_cast<const char*>(p.k) +
+                      ((int64_t)page * p.k_sp + (int64_t)slot * p.k_ss + (int64_t)s.g * p.k_sh) * ELT);
+    vb = wave_uniform(reinterpret_cast<const char*>(p.v) +
+                      ((int64_t)page * p.v_sp + (int64_t)slot * p.v_ss + (int64_t)s.g * p.v_sh) * ELT);
+  }
   __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s, int tile) {
     J0 = wave_uniform(tile) * kUnitKeys;
     nvalid = wave_uniform(min(kUnitKeys, s.ctx - J0));
     kss = (uint32_t)(p.k_ss * ELT);
     vss = (uint32_t)(p.v_ss * ELT);
     if constexpr (FAST) {
-      const int page = page_of(p, s, J0);
+      page = page_of(p, s, J0);
       const int slot = J0 & (p.page_size - 1);
       kb = reinterpret_cast<const char*>(p.k) + ((int64_t)page * p.k_sp + (int64_t)slot * p.k_ss + (int64_t)s.g * p.k_sh) * ELT;
       vb = reinterpret_cast<const char*>(p.v) + ((int64_t)page * p.v_sp + (int64_t)slot * p.v_ss + (int64_t)s.g * p.v_sh) * ELT;
@@ -197,6 +218,19 @@ struct Tile {
     }
   }
 };
+
+// Scales of a tile whose physical page is known (page_size >= 64).
+template <int KIND>
+__device__ __forceinline__ float kscale_at_page(const KParams& p, const SeqCtx& s, int page, float* vsc) {
+  if constexpr (KIND != KIND_F8) {
+    *vsc = 1.f;
+    return 1.f;
+  } else {
+    const int i = p.scale_mode == 2 ? page * p.Hkv + s.g : 0;
+    *vsc = p.v_scale[i];
+    return p.k_scale[i];
+  }
+}
 
 template <int KIND>
 __device__ __forceinline__ float kscale_of(const KParams& p, const SeqCtx& s, int key, float* vsc) {
@@ -648,17 +682,12 @@ __device__ __forceinline__ void mask_scores(f32x4 (&sc)[4], const ElemMask& em, 
   }
 }
 
-// Q operands of a small Q-block, either staged in LDS (shared by the four
-// waves of one segment) or held in registers (one wave streaming Q-blocks).
+// Q operands of a small Q-block staged in LDS: element ks * 64 + lane holds
+// lane's operand of K-step ks.
 template <int KIND, int D>
 struct QFromLds {
   const typename QKOpT<KIND>::T* q;
   __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int lane) const { return q[ks * 64 + lane]; }
-};
-template <int KIND, int D>
-struct QFromRegs {
-  const typename QKOpT<KIND>::T* q;   // the wave's own operands, indexed by K-step
-  __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int) const { return q[ks]; }
 };
 
 template <int KIND, int D, bool FAST, class QSrc>
@@ -671,7 +700,9 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
   const int h = lane >> 4;
   const int J0 = tc.J0;
   float vsc;
-  const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
+  float ksc;
+  if constexpr (FAST) ksc = kscale_at_page<KIND>(p, s, tc.page, &vsc);
+  else ksc = kscale_of<KIND>(p, s, J0, &vsc);
   if (p.bm) {
     const int kt = J0 / p.bm_tile, qt = rm.pos / p.bm_tile;
     rm.bit = kt < p.bm_nk && qt < p.bm_nq &&
@@ -857,6 +888,256 @@ __device__ void small_segment(const KParams& p, const QBlock& x, int t_lo, int t
       *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
       *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
       if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// A run of consecutive small Q-blocks inside one worker's range (no block
+// mask).  The run's units are cut into four contiguous quarters, one per
+// wave; each wave streams its tiles without pause across Q-block boundaries
+// (the double-buffered loads of the next tile — K, V and its Q-block's Q
+// rows — overlap the current tile's math).  A Q-block lying wholly inside a
+// wave's quarter is written out directly; only the first and last Q-block of
+// a quarter can be cut, and those pieces are merged once, through LDS, when
+// the run ends.  Per-segment splitting would instead drain every wave's
+// pipeline and synchronise the workgroup at each of the many short decode
+// Q-blocks of a ragged batch.
+// ---------------------------------------------------------------------------
+template <int KIND, int D, bool FAST>
+struct StreamRec {
+  int q, t_lo;
+  QBlock x;
+  Tile<Cfg<KIND, D>::ELT, FAST> t;
+  SmallRegs<KIND, D> r;
+};
+
+// Where the prefetch stands: the Q-block of the last prepared unit, its unit
+// range [S, E), and a window of 64 page-table entries of its sequence held one
+// per lane, so that a tile's page costs a register read instead of a
+// dependent scalar memory load.  Q rows for a record that enters a new
+// Q-block are loaded into `qtmp` ahead of that record's K/V loads and moved to
+// the record's LDS slot at the next prepare, by when they have arrived
+// without waiting for any K/V load.
+template <int KIND, int D>
+struct StreamCursor {
+  int q, S, E, t_lo;
+  QBlock x;
+  int pbase;     // page-table index held by lane 0 of vpage
+  int vpage;
+  int qpend;     // LDS slot waiting for qtmp, or -1
+  typename QKOpT<KIND>::T qtmp[Cfg<KIND, D>::KSQ];
+};
+
+template <int KIND, int D>
+struct StashLayout {   // 8 pieces (2 per wave): m[16], l[16], acc[16][D] (raw), tag
+  static constexpr int PIECES = 2 * kWaves;
+  static constexpr int M = 0, Lf = PIECES * 16, ACC = 2 * PIECES * 16;
+  static constexpr int FLOATS = ACC + PIECES * 16 * D;
+  static constexpr int BYTES = FLOATS * 4 + PIECES * 4;
+};
+
+template <int KIND, int D, bool FAST>
+__device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor<KIND, D>& c, StreamRec<KIND, D, FAST>& rec,
+                                               typename QKOpT<KIND>::T* qslots, int slot, int u, int n, int h,
+                                               int lane) {
+  using C = Cfg<KIND, D>;
+  if (c.qpend >= 0) {                                    // Q rows of an earlier record: now in registers
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks) qslots[(c.qpend * C::KSQ + ks) * 64 + lane] = c.qtmp[ks];
+    c.qpend = -1;
+  }
+  if (u >= c.E) {                                        // next Q-block (rare: scalar loads)
+    int q = c.q;
+    while (p.unit_prefix[q + 1] <= u) ++q;
+    c.q = wave_uniform(q);
+    c.x = load_qblock(p, c.q);
+    c.S = wave_uniform(p.unit_prefix[c.q]);
+    c.E = wave_uniform(p.unit_prefix[c.q + 1]);
+    int t_hi;
+    qblock_tiles(p, c.x.ctx, c.x.pos_lo, c.x.pos_hi, c.t_lo, t_hi);
+    c.pbase = -(1 << 30);
+  }
+  const QBlock& x = c.x;
+  SeqCtx s{x.b, x.g, x.ctx, c.t_lo, p.bt + (int64_t)x.b * p.bt_stride};
+  if (rec.q != c.q) {                                    // the record enters a new Q-block: its Q rows first
+    // rows past the Q-block re-read row 0: finite scores that are never written
+    const int r = n < x.rows ? n : 0;
+    const int tok = x.q0 + x.t0 + r / p.G, head = x.g * p.G + r % p.G;
+    const char* at = reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT;
+    __builtin_assume(at != nullptr);
+    load_qk_row<KIND, D>(at, h, c.qtmp);
+    c.qpend = slot;
+    rec.q = c.q;
+    rec.x = x;
+    rec.t_lo = c.t_lo;
+  }
+  const int tile = c.t_lo + (u - c.S);
+  if constexpr (FAST) {
+    const int idx = (tile * kUnitKeys) >> p.page_shift;
+    if ((unsigned)(idx - c.pbase) >= 64u) {              // refill the page window
+      c.pbase = idx;
+      int v = s.bt_row[min(idx + lane, p.max_pages - 1)];
+      // complete the load here, where it is rare: a later read of the window
+      // would otherwise wait for every load in flight, tiles included
+      asm volatile("" : "+v"(v));
+      c.vpage = v;
+    }
+    int page = idx < p.max_pages ? __builtin_amdgcn_readlane(c.vpage, idx - c.pbase) : -1;
+    if ((unsigned)page >= (unsigned)p.num_pages) {
+      p.hdr[H_ERROR] = E_PAGE;
+      page = 0;
+    }
+    rec.t.init_at_page(p, s, tile, page);
+  } else {
+    rec.t.init(p, s, tile);
+  }
+  small_load_k<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+  small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+}
+
+template <int KIND, int D, bool FAST>
+__device__ void small_range(const KParams& p, int vw, int L, int a, int b, char* smem) {
+  using C = Cfg<KIND, D>;
+  using SL = StashLayout<KIND, D>;
+  constexpr int MD = C::MD;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, h = lane >> 4;
+  float* stash = reinterpret_cast<float*>(smem);
+  int* tags = reinterpret_cast<int*>(smem + SL::FLOATS * 4);
+  using QT = typename QKOpT<KIND>::T;
+  QT* qslots = reinterpret_cast<QT*>(smem + C::QSLOTS_OFF) + wave * 2 * C::KSQ * 64;
+  if (lane < 2) tags[2 * wave + lane] = -1;
+  const int cnt = b - a;
+  const int wa = wave_uniform(a + (cnt * wave) / kWaves), wb = wave_uniform(a + (cnt * (wave + 1)) / kWaves);
+
+  if (wa < wb) {
+    // the current piece: its Q-block, state and row mask
+    int cur_q = -1;
+    QBlock cx;
+    RowMask rm;
+    int pos_min = 0, left_max = 0;
+    WaveState<KIND, D, 1> st;
+    st.init();
+    auto finish = [&]() {
+      float l = st.lsum[0];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      const int S = p.unit_prefix[cur_q], E = p.unit_prefix[cur_q + 1];
+      if (S >= wa && E <= wb) {                          // whole Q-block in this quarter: final output
+        if (n < cx.rows) {
+          const bool empty = !(l > 0.f);
+          write_row<KIND, D>(p, cx, n, h, st.acc[0], empty ? 0.f : 1.f / l,
+                             empty ? kNegInf : (st.m2[0] + log2f(l)) * kLn2, true, 0);
+        }
+      } else {                                           // cut piece: stash raw state for the merge
+        const int k = 2 * wave + (S < wa ? 0 : 1);
+        if (lane == 0) tags[k] = cur_q;
+        if (h == 0) {
+          stash[SL::M + k * 16 + n] = st.m2[0];
+          stash[SL::Lf + k * 16 + n] = l;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int md = 0; md < MD; ++md) stash[SL::ACC + (k * 16 + n) * D + out_dim<KIND, D>(h, j, md)] = st.acc[0][md][j];
+      }
+    };
+    auto consume = [&](const StreamRec<KIND, D, FAST>& rec, int slot) {
+      if (rec.q != cur_q) {
+        if (cur_q >= 0) finish();
+        cur_q = rec.q;
+        cx = rec.x;
+        st.init();
+        const int r = n < cx.rows ? n : 0;
+        rm.pos = cx.ctx - cx.ql + cx.t0 + r / p.G;
+        rm.left = p.window > 0 ? window_left(p, rm.pos) : 0;
+        rm.bit = true;
+        pos_min = cx.pos_lo;
+        left_max = p.window > 0 ? window_left(p, cx.pos_hi) : 0;
+      }
+      SeqCtx s{cx.b, cx.g, cx.ctx, rec.t_lo, p.bt + (int64_t)cx.b * p.bt_stride};
+      small_compute<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromLds<KIND, D>{qslots + slot * C::KSQ * 64}, rm, 0,
+                                   pos_min, left_max, st, lane);
+    };
+    // the Q-block of the first unit: last q with unit_prefix[q] <= wa
+    int lo = 0, hi = p.hdr[H_NQB] - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.unit_prefix[mid] <= wa) lo = mid; else hi = mid - 1;
+    }
+    StreamCursor<KIND, D> c;
+    c.q = wave_uniform(lo);
+    c.E = -1;                                            // forces the Q-block load on the first unit
+    c.qpend = -1;
+    StreamRec<KIND, D, FAST> A, B;
+    A.q = -1;
+    B.q = -1;
+    // Every consume is preceded by a prepare of the other record (past the
+    // end it repeats the last unit, an L2 hit), so the loads in flight at
+    // each wait are the same on every path and the prepare also moves the
+    // consumed record's Q rows into LDS.
+    const int last = wb - 1;
+    stream_prepare<KIND, D, FAST>(p, c, A, qslots, 0, wa, n, h, lane);
+    for (int u = wa; u < wb; u += 2) {
+      stream_prepare<KIND, D, FAST>(p, c, B, qslots, 1, min(u + 1, last), n, h, lane);
+      consume(A, 0);
+      if (u + 1 >= wb) break;
+      stream_prepare<KIND, D, FAST>(p, c, A, qslots, 0, min(u + 2, last), n, h, lane);
+      consume(B, 1);
+    }
+    finish();
+  }
+  __syncthreads();
+
+  // merge the cut pieces, one Q-block at a time (at most 8 pieces)
+  constexpr int TPR = D / 8;
+  for (int k = 0; k < SL::PIECES; ++k) {
+    const int q = tags[k];
+    if (q < 0) continue;
+    bool first = true;
+    for (int j = 0; j < k; ++j) first = first && tags[j] != q;
+    if (!first) continue;
+    const QBlock x = load_qblock(p, q);
+    const bool final_out = p.n_splits[q] == 1;
+    const int slot = final_out ? 0 : p.slot_base[q] + (vw - p.unit_prefix[q] / L);
+    for (int idx = threadIdx.x; idx < x.rows * TPR; idx += kThreads) {
+      const int row = idx / TPR, d0 = (idx % TPR) * 8;
+      float M = kNegInf;
+      for (int j = k; j < SL::PIECES; ++j)
+        if (tags[j] == q) M = fmaxf(M, stash[SL::M + j * 16 + row]);
+      float Ls = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (M != kNegInf) {
+        for (int j = k; j < SL::PIECES; ++j) {
+          if (tags[j] != q) continue;
+          const float c = __builtin_amdgcn_exp2f(stash[SL::M + j * 16 + row] - M);
+          Ls += stash[SL::Lf + j * 16 + row] * c;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] += stash[SL::ACC + (j * 16 + row) * D + d0 + i] * c;
+        }
+      }
+      const bool empty = !(Ls > 0.f);
+      const float inv = empty ? 0.f : 1.f / Ls;
+      const float lse = empty ? kNegInf : (M + log2f(Ls)) * kLn2;
+      const int tk = x.q0 + x.t0 + row / p.G, hd = x.g * p.G + row % p.G;
+      if (final_out) {
+        if constexpr (KIND == KIND_F32) {
+          float* dst = reinterpret_cast<float*>(p.out) + tk * p.o_st + hd * p.o_sh + d0;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        } else {
+          char* dst = reinterpret_cast<char*>(p.out) + (tk * p.o_st + hd * p.o_sh + d0) * 2;
+          *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                                                 pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+        }
+        if (d0 == 0) p.lse[tk * p.l_st + hd * p.l_sh] = lse;
+      } else {
+        float* dst = p.part_o + ((int64_t)slot * kLargeRows + row) * D + d0;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+      }
     }
   }
   __syncthreads();
@@ -1263,6 +1544,21 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(KParams p) {
       if (nq == 0) { ++q; continue; }
       const int u0 = a - S, u1 = min(b_end, S + nq) - S;
       const QBlock x = load_qblock(p, q);
+      if (x.rows <= kSmallMaxRows && p.bm == nullptr) {
+        // the maximal run of small Q-blocks from here, inside this worker's range
+        int run_end = S + u1, qq = q + 1;
+        while (run_end < b_end && qq < n_qb) {
+          const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[qq];
+          if (wave_uniform(d.w) * p.G > kSmallMaxRows) break;
+          run_end = min(b_end, p.unit_prefix[qq + 1]);
+          ++qq;
+        }
+        run_end = wave_uniform(run_end);
+        small_range<KIND, D, FAST>(p, vw, L, a, run_end, smem);
+        a = run_end;
+        while (q < n_qb && p.unit_prefix[q + 1] <= a) ++q;
+        continue;
+      }
       int t_lo = 0, t_hi = 0;
       qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, t_lo, t_hi);
       const bool final_out = p.n_splits[q] == 1;
