@@ -102,15 +102,25 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload):
-    """HBM bytes per attention launch from committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def profile_summary(workload):
+    """The JSON block of profiles/attention_kernel_<workload>.md, or None."""
+    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload}.md")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("source_sha") != source_sha():
+    text = open(path).read()
+    a = text.find("```json")
+    if a < 0:
+        return None
+    b = text.find("```", a + 7)
+    return json.loads(text[a + 7:b])
+
+
+def traffic_for(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (scaled by the copy-kernel calibration), if they were taken
+    on the current kernel source; else None."""
+    t = profile_summary(workload)
+    if not t or t.get("source_sha") != source_sha():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -140,36 +150,33 @@ def time_workload(batch, steps, warmup):
     return ms, {"assign": a / n, "attention": att / n, "combine": c / n}, (g, out, lse, ws)
 
 
-def cpu_baseline(batch, budget_s=15.0):
-    """The oracle on the first sequences of the batch until ~budget_s of CPU work."""
+def cpu_baseline(batch, budget_s=12.0):
+    """The oracle, one sequence at a time in batch order (wrapping round), until
+    ~budget_s of CPU work; throughput in the same algorithmic GB/s."""
     from threadpoolctl import threadpool_limits
     from tests.oracle_helpers import run_oracle
-    qsl = batch.query_start_loc.numpy()
-    done_rows = np.zeros(batch.total_q, bool)
-    t_total = 0.0
-    nseq = 0
+    qsl = batch.query_start_loc.numpy().astype(np.int64)
+    ctx_all = batch.seq_lens.numpy().astype(np.int64)
+    d, Hq, Hkv = batch.head_dim, batch.num_q_heads, batch.num_kv_heads
+    elt = {"f32": 4, "bf16": 2, "e4m3": 1}[batch.kind]
+    t_total, by, calls, keys = 0.0, 0, 0, 0
     with threadpool_limits(limits=1):
-        for s in range(batch.num_seqs):
+        while t_total < budget_s:
+            s = calls % batch.num_seqs
             rows = np.zeros(batch.total_q, bool)
             rows[qsl[s]:qsl[s + 1]] = True
             t = time.perf_counter()
             run_oracle(batch, rows=rows)
             t_total += time.perf_counter() - t
-            done_rows |= rows
-            nseq += 1
-            if t_total >= budget_s:
-                break
-    # algorithmic bytes of the sampled sequences
-    ctx = batch.seq_lens.numpy().astype(np.int64)[:nseq]
-    d, Hq, Hkv = batch.head_dim, batch.num_q_heads, batch.num_kv_heads
-    elt = {"f32": 4, "bf16": 2, "e4m3": 1}[batch.kind]
-    nq = int(qsl[nseq])
-    by = int(ctx.sum()) * Hkv * d * elt * 2 + nq * Hq * d * (elt + 2) + nq * Hq * 4 + \
-        int(((ctx + batch.page_size - 1) // batch.page_size).sum()) * 4
-    return {"value": by / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {nseq} of {batch.num_seqs} sequences ({int(ctx.sum())} keys, {nq} query rows) "
-                      f"of the same decode batch, fp64 NumPy oracle, BLAS limited to 1 thread, "
-                      f"{t_total:.1f} s"}
+            nq, c = int(qsl[s + 1] - qsl[s]), int(ctx_all[s])
+            by += c * Hkv * d * elt * 2 + nq * Hq * d * (elt + 2) + nq * Hq * 4 + \
+                (c + batch.page_size - 1) // batch.page_size * 4
+            keys += c
+            calls += 1
+    return {"value": round(by / t_total / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} single-sequence oracle calls over the same decode batch in order "
+                      f"({keys} keys, {by / 1e9:.3f} GB algorithmic), fp64 NumPy, BLAS limited to one "
+                      f"thread, {t_total:.1f} s"}
 
 
 WORKLOADS = {
@@ -204,6 +211,140 @@ def leg(name, steps, warmup):
     return batch, by, flops, ms, kms
 
 
+COPY_CALIBRATION_BYTES = 1 << 30
+
+
+def copy_calibration(launches=5):
+    """Plain device-to-device copies of COPY_CALIBRATION_BYTES: the reference
+    for scaling FETCH_SIZE / WRITE_SIZE counter readings to bytes."""
+    import torch
+    src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device="cuda:0")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_CALIBRATION_BYTES, "launches": launches}), flush=True)
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_per_dispatch(directory, counter, name_pred):
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(directory, "counter_collection.csv")
+            if r["Counter_Name"] == counter and name_pred(r["Kernel_Name"])]
+    return vals
+
+
+def summarize_profiles(d):
+    """Turn the rocprofv3 CSV output of the profiling commands (listed in
+    <d>/commands.txt) into the text summaries under profiles/."""
+    cmds = open(os.path.join(d, "commands.txt")).read().strip()
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    is_copy = lambda n: "copy" in n.lower()
+    is_att = lambda n: "attention_kernel" in n
+    # copy calibration: counter KiB per dispatch against the known byte count
+    cf = _counter_per_dispatch(os.path.join(d, "copy_fetch"), "FETCH_SIZE", is_copy)
+    cw = _counter_per_dispatch(os.path.join(d, "copy_write"), "WRITE_SIZE", is_copy)
+    cf_med, cw_med = float(np.median(cf)), float(np.median(cw))
+    f_scale = COPY_CALIBRATION_BYTES / (cf_med * 1024.0)
+    w_scale = COPY_CALIBRATION_BYTES / (cw_med * 1024.0)
+    with open(os.path.join(out_dir, "copy_calibration.md"), "w") as f:
+        f.write("# FETCH_SIZE / WRITE_SIZE calibration on a plain copy kernel\n\n")
+        f.write(f"Copy of {COPY_CALIBRATION_BYTES} bytes (1 GiB), {len(cf)} dispatches.\n\n")
+        f.write(f"| counter | median KiB per dispatch | bytes it stands for | scale |\n|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {cf_med:.1f} | {COPY_CALIBRATION_BYTES} | {f_scale:.4f} |\n")
+        f.write(f"| WRITE_SIZE | {cw_med:.1f} | {COPY_CALIBRATION_BYTES} | {w_scale:.4f} |\n\n")
+        f.write("Commands:\n\n```\n" + cmds + "\n```\n")
+    # full kernel stats of the default bench command
+    stats = _csv_rows(os.path.join(d, "trace"), "kernel_stats.csv")
+    trace = _csv_rows(os.path.join(d, "trace"), "kernel_trace.csv")
+    bench_line = [json.loads(x) for x in open(os.path.join(d, "bench_trace.json")).read().splitlines()
+                  if x.startswith("{")][-1]
+    att = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+           for r in trace if is_att(r["Kernel_Name"])]
+    att.sort()
+    steps, warmup = bench_line["steps"], bench_line["warmup"]
+    n_dec = 1 + warmup + steps                       # run_batch once, warmup, timed steps
+    legs = {bench_line["config"]["workload"]: att[:n_dec]}
+    if "prefill" in bench_line:
+        n_pre = 1 + warmup + max(5, steps // 2)
+        legs[bench_line["prefill"]["workload"]] = att[n_dec:n_dec + n_pre]
+    with open(os.path.join(out_dir, "bench_default_kernel_stats.md"), "w") as f:
+        f.write("# rocprofv3 kernel statistics of the default bench command\n\n")
+        f.write("| kernel | calls | average ns | min ns | max ns | % |\n|---|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                    f"{r['MaxNs']} | {r['Percentage']} |\n")
+        f.write("\nThe attention kernel serves both legs under one name; the per-dispatch trace splits them "
+                "in launch order (first call, warmup, timed steps of each leg):\n\n")
+        f.write("| leg | dispatches | average ns (timed steps) | bench HIP-event ms |\n|---|---|---|---|\n")
+        for wl, ds in legs.items():
+            timed = [x[1] for x in ds[-(steps if wl == bench_line['config']['workload'] else max(5, steps // 2)):]]
+            ev = bench_line["kernels_ms"]["attention"] if wl == bench_line["config"]["workload"] \
+                else bench_line["prefill"]["kernels_ms"]["attention"]
+            f.write(f"| {wl} | {len(ds)} | {np.mean(timed):.0f} | {ev} |\n")
+        f.write("\nCommands:\n\n```\n" + cmds + "\n```\n")
+    # per-workload counter summaries
+    for wl in sorted({x[len("fetch_"):] for x in os.listdir(d)
+                      if x.startswith("fetch_") and os.path.isdir(os.path.join(d, x))}):
+        fv = _counter_per_dispatch(os.path.join(d, f"fetch_{wl}"), "FETCH_SIZE", is_att)
+        wv = _counter_per_dispatch(os.path.join(d, f"write_{wl}"), "WRITE_SIZE", is_att)
+        fb = float(np.median(fv)) * 1024.0 * f_scale
+        wb = float(np.median(wv)) * 1024.0 * w_scale
+        timed = None
+        if wl in legs:
+            k = steps if wl == bench_line["config"]["workload"] else max(5, steps // 2)
+            timed = float(np.mean([x[1] for x in legs[wl][-k:]]))
+        batch = WORKLOADS[wl]()
+        pairs, keys = visible_pairs_and_keys(batch)
+        alg = algorithmic_bytes(batch, keys)
+        summary = {"workload": wl, "kernel": "attention_kernel", "source_sha": source_sha(),
+                   "fetch_kib_median": float(np.median(fv)), "write_kib_median": float(np.median(wv)),
+                   "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                   "hbm_bytes_per_launch": int(fb + wb), "algorithmic_bytes": int(alg),
+                   "traffic_over_algorithmic": round((fb + wb) / alg, 4),
+                   "avg_ns_rocprof": None if timed is None else round(timed),
+                   "flops": 4.0 * batch.head_dim * pairs}
+        mf = os.path.join(d, f"mfma_{wl}")
+        if os.path.isdir(mf):
+            rows = _csv_rows(mf, "counter_collection.csv")
+            agg = {}
+            for r in rows:
+                if is_att(r["Kernel_Name"]):
+                    agg.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            summary["mfma_counters_median"] = {k: float(np.median(v)) for k, v in agg.items()}
+        with open(os.path.join(out_dir, f"attention_kernel_{wl}.md"), "w") as f:
+            f.write(f"# attention_kernel on {wl}\n\n")
+            f.write(f"HBM traffic per launch: FETCH_SIZE {summary['fetch_kib_median']:.0f} KiB x {f_scale:.3f} + "
+                    f"WRITE_SIZE {summary['write_kib_median']:.0f} KiB x {w_scale:.3f} = "
+                    f"{summary['hbm_bytes_per_launch'] / 1e6:.1f} MB against {alg / 1e6:.1f} MB algorithmic "
+                    f"({summary['traffic_over_algorithmic']:.3f}x).\n\n")
+            if timed is not None:
+                f.write(f"Average duration of the timed launches in the kernel trace: {timed / 1e3:.1f} us.\n\n")
+            mine = "\n".join(c for c in cmds.splitlines()
+                             if f" {wl} " in c + " " or "--copy-calibration" in c or "--kernel-trace" in c)
+            f.write("```json\n" + json.dumps(summary, indent=1) + "\n```\n\nCommands (the copy runs calibrate "
+                    "the counters, the kernel-trace run gives the durations):\n\n```\n" + mine + "\n```\n")
+        del batch
+    print("wrote summaries to", out_dir)
+
+
+def profile_leg(name, steps, warmup):
+    """One workload only (for counter runs): prints its timing as JSON."""
+    batch, by, flops, ms, kms = leg(name, steps, warmup)
+    print(json.dumps({"workload": name, "ms_per_step": ms, "kernels_ms": kms}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,13 +354,28 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill_bf16_dense", choices=sorted(WORKLOADS) + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", default="", help="comma-separated extra workloads to time (reported under 'also')")
+    ap.add_argument("--profile-leg", default=None, choices=sorted(WORKLOADS),
+                    help="time only this workload (for rocprofv3 counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run plain 1 GiB device copies (counter calibration) and exit")
+    ap.add_argument("--summarize-profiles", default=None, metavar="DIR",
+                    help="write profiles/*.md from the rocprofv3 CSV output under DIR (CPU only)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.profile_leg:
+        profile_leg(args.profile_leg, args.steps, args.warmup)
+        return
 
     batch, by, flops, ms, kms = leg(args.workload, args.steps, args.warmup)
     gbs = by / (ms * 1e-3) / 1e9
