@@ -2,6 +2,7 @@
 // the three launches (Assign -> split-K attention -> Combine) on the caller's
 // stream, and optional per-launch event timing.  See include/paged_attn.h.
 #include <hip/hip_runtime.h>
+#include <cmath>
 
 #include <cstring>
 #include <mutex>
@@ -53,7 +54,7 @@ pa_status default_workers(int32_t* out) {
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e);
-  *out = cus;                  // one persistent workgroup per compute unit
+  *out = 2 * cus;              // two persistent workgroups per compute unit
   return PA_OK;
 }
 
@@ -72,7 +73,7 @@ pa_status check_params(const pa_params* p) {
   if (p->num_workers < 0 || p->split_min_units < 0 || p->force_split_units < 0 || p->max_partial_slots < 0)
     return PA_ERR_INVALID_ARG;
   if (p->flags != 0) return PA_ERR_INVALID_ARG;
-  if (!(p->softmax_scale == p->softmax_scale)) return PA_ERR_INVALID_ARG;   // NaN
+  if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
   return PA_OK;
 }
 
@@ -165,7 +166,7 @@ pa_status paged_attn_device_info(int32_t device, pa_device_info* info) {
   std::memset(info, 0, sizeof(*info));
   info->compute_units = prop.multiProcessorCount;
   info->lds_bytes_per_workgroup = static_cast<int32_t>(prop.sharedMemPerBlock);
-  info->default_workers = prop.multiProcessorCount;
+  info->default_workers = 2 * prop.multiProcessorCount;
   std::strncpy(info->arch, prop.gcnArchName, sizeof(info->arch) - 1);
   return PA_OK;
 }

@@ -59,13 +59,13 @@ struct Cfg {
   static constexpr int MERGE = kWaves * kSmallMaxRows * (D + 2) * 4;  // small-path wave merge
   static constexpr int QOFF = (MERGE + 255) / 256 * 256;               // small-path Q operands
   static constexpr int QBYTES = KSQ * 64 * (KIND == KIND_F32 ? 4 : KIND == KIND_BF16 ? 16 : 8);
-  // small_range: merge stash of 8 cut pieces, then two Q-operand slots per wave
+  // small_range: merge stash of 8 cut pieces (m, l, raw O per row) and tags
   static constexpr int STASH = (2 * kWaves) * (32 + 16 * D) * 4 + 2 * kWaves * 4;
-  static constexpr int QSLOT = 64 * KSQ * (KIND == KIND_F32 ? 4 : KIND == KIND_BF16 ? 16 : 8);
-  static constexpr int QSLOTS_OFF = (STASH + 255) / 256 * 256;
-  static constexpr int STREAM = QSLOTS_OFF + 2 * kWaves * QSLOT;
   static constexpr int BODY0 = 2 * STAGE > QOFF + QBYTES ? 2 * STAGE : QOFF + QBYTES;
-  static constexpr int LDS = (BODY0 > STREAM ? BODY0 : STREAM) + kMaskListCap * 2;
+  static constexpr int LDS = (BODY0 > STASH ? BODY0 : STASH) + kMaskListCap * 2;
+  // workgroups per compute unit: two (so that each SIMD runs two waves) where
+  // half the LDS suffices, else one
+  static constexpr int OCC = LDS <= 80 * 1024 ? 2 : 1;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -353,34 +353,44 @@ struct WaveState {
   }
 };
 
-// Softmax update of one row-block: s2 holds log2-domain scores (masked = -inf)
-// and is overwritten by the probabilities.
+// Online softmax update of one row-block.  `s` holds raw scores Q.K (masked =
+// -inf) and is overwritten by the probabilities 2^(cs * s - m); cs > 0 is the
+// log2-domain score scale.  The reference max m of a row moves only when the
+// row's running max exceeds it by more than kRescaleSlack, so in the common
+// case the accumulator is not rescaled at all and the probabilities stay
+// below 2^kRescaleSlack (exact in the result: l and O use the same m).
+constexpr float kRescaleSlack = 8.f;
+
 template <int KIND, int D, int NB>
-__device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int nb, f32x4 (&s2)[4]) {
+__device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int nb, f32x4 (&s)[4], float cs) {
   float mx = kNegInf;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s2[mb][j]);
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mb][j]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m2[nb], mx);
-  const bool dead = m_new == kNegInf;                   // nothing visible so far
-  const float alpha = dead ? 1.f : __builtin_amdgcn_exp2f(st.m2[nb] - m_new);
-  const float mref = dead ? 0.f : m_new;
+  const float m_cand = mx == kNegInf ? kNegInf : mx * cs;
+  const bool grow = m_cand > st.m2[nb] + kRescaleSlack;
+  if (__ballot(grow) != 0) {                            // wave-uniform, rare after the first tiles
+    const float m_new = grow ? m_cand : st.m2[nb];
+    const float alpha = st.m2[nb] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st.m2[nb] - m_new);
+    st.lsum[nb] *= alpha;
+#pragma unroll
+    for (int md = 0; md < Cfg<KIND, D>::MD; ++md) st.acc[nb][md] *= alpha;
+    st.m2[nb] = m_new;
+  }
+  const float nmref = st.m2[nb] == kNegInf ? 0.f : -st.m2[nb];
   float sum = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float e = __builtin_amdgcn_exp2f(s2[mb][j] - mref);
-      s2[mb][j] = e;
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][j], cs, nmref));
+      s[mb][j] = e;
       sum += e;
     }
-  st.lsum[nb] = st.lsum[nb] * alpha + sum;
-  st.m2[nb] = m_new;
-#pragma unroll
-  for (int md = 0; md < Cfg<KIND, D>::MD; ++md) st.acc[nb][md] *= alpha;
+  st.lsum[nb] += sum;
 }
 
 // P^T operand (bf16) of PV K-step ks2: slot t = key 32 ks2 + 16 (t / 4) + 4 h + t % 4.
@@ -584,16 +594,13 @@ template <int KIND, int D, bool FAST>
 __device__ __forceinline__ void small_load_k(const KParams& p, const SeqCtx& s, const Tile<Cfg<KIND, D>::ELT, FAST>& t,
                                              SmallRegs<KIND, D>& r, int n, int h) {
   if constexpr (FAST) {
-    if (t.nvalid == kUnitKeys) {
-      const uint32_t lane = (uint32_t)n * t.kss + lane_dim_bytes<KIND>(h);
+    // The tile lies inside one page, so rows past the sequence end are still
+    // cache memory: read them unclamped (their scores are masked to -inf by
+    // select, never used).  Uniform row bases + one lane offset keep every
+    // load in the scalar-base form.
+    const uint32_t lane = (uint32_t)n * t.kss + lane_dim_bytes<KIND>(h);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) bload_qk<KIND, D>(t.kb, lane, 16 * mb * t.kss, r.kA[mb]);
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        bload_qk<KIND, D>(t.kb, (uint32_t)min(16 * mb + n, t.nvalid - 1) * t.kss + lane_dim_bytes<KIND>(h), 0u,
-                          r.kA[mb]);
-    }
+    for (int mb = 0; mb < 4; ++mb) bload_qk<KIND, D>(t.kb + 16 * mb * t.kss, lane, 0u, r.kA[mb]);
   } else {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) load_qk_row<KIND, D>(t.krow(p, s, 16 * mb + n), h, r.kA[mb]);
@@ -634,21 +641,20 @@ __device__ __forceinline__ void small_load_v(const KParams& p, const SeqCtx& s, 
   } else {
     // piece (ks2, pc): row 32 ks2 + 16 (pc / 4) + 4 h + pc % 4, dims MD n ..
     if constexpr (FAST) {
-      if (t.nvalid == kUnitKeys) {
-        const uint32_t lane = (uint32_t)(4 * h) * t.vss + MD * n * ELT;
+      // unclamped as for K; rows past the sequence end may hold anything (NaN
+      // included) and would poison O through 0 * NaN, so they are zeroed
+      const uint32_t lane = (uint32_t)(4 * h) * t.vss + MD * n * ELT;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc)
+          r.vr[ks2][pc] = bload_v<KIND, MD>(t.vb + (32 * ks2 + 16 * (pc >> 2) + (pc & 3)) * t.vss, lane, 0u);
+      if (t.nvalid < kUnitKeys) {                        // uniform: the sequence's last tile
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
           for (int pc = 0; pc < 8; ++pc)
-            r.vr[ks2][pc] = bload_v<KIND, MD>(t.vb, lane, (32 * ks2 + 16 * (pc >> 2) + (pc & 3)) * t.vss);
-      } else {
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-          for (int pc = 0; pc < 8; ++pc) {
-            const int kt = min(32 * ks2 + 16 * (pc >> 2) + 4 * h + (pc & 3), t.nvalid - 1);
-            r.vr[ks2][pc] = bload_v<KIND, MD>(t.vb, (uint32_t)kt * t.vss + MD * n * ELT, 0u);
-          }
+            if (32 * ks2 + 16 * (pc >> 2) + 4 * h + (pc & 3) >= t.nvalid) r.vr[ks2][pc] = {};
       }
     } else {
 #pragma unroll
@@ -682,12 +688,17 @@ __device__ __forceinline__ void mask_scores(f32x4 (&sc)[4], const ElemMask& em, 
   }
 }
 
-// Q operands of a small Q-block staged in LDS: element ks * 64 + lane holds
-// lane's operand of K-step ks.
+// Q operands of a small Q-block, staged in LDS (element ks * 64 + lane holds
+// lane's operand of K-step ks) or held in the lane's registers.
 template <int KIND, int D>
 struct QFromLds {
   const typename QKOpT<KIND>::T* q;
   __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int lane) const { return q[ks * 64 + lane]; }
+};
+template <int KIND, int D>
+struct QFromRegs {
+  const typename QKOpT<KIND>::T* q;
+  __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int) const { return q[ks]; }
 };
 
 template <int KIND, int D, bool FAST, class QSrc>
@@ -722,14 +733,12 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
   const bool full = unit_is_full(p, J0, tc.nvalid, pos_min, left_max, lmk);
   float cs = p.sm_log2;
   if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) sc[mb] *= cs;
   if (!full) {
     ElemMask em;
     em.init(p, rm, J0, tc.nvalid, lmk);
     mask_scores(sc, em, h);
   }
-  softmax_update<KIND, D, 1>(st, 0, sc);
+  softmax_update<KIND, D, 1>(st, 0, sc, cs);
   // O^T += V^T P^T
   if constexpr (KIND == KIND_F32) {
 #pragma unroll
@@ -753,8 +762,8 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
   }
 }
 
-// Double-buffered: the K/V loads of tile u + 1 are in flight while tile u is
-// computed (two static register sets, the loop unrolled by two).
+// One tile in flight per wave: the second wave on each SIMD (two workgroups
+// per compute unit) computes while this one waits for its loads.
 template <int KIND, int D, bool FAST>
 __device__ __forceinline__ void small_run(const KParams& p, const SeqCtx& s, const QBlock& x, const short* list,
                                           int c0, int t_lo, int a, int b,
@@ -763,28 +772,15 @@ __device__ __forceinline__ void small_run(const KParams& p, const SeqCtx& s, con
                                           int lane) {
   using C = Cfg<KIND, D>;
   const int n = lane & 15, h = lane >> 4;
-  auto tile_of = [&](int u) {   // wave-uniform: keeps tile addressing in scalar registers
-    return __builtin_amdgcn_readfirstlane(p.bm ? (int)list[u - c0] : t_lo + u);
-  };
-  Tile<C::ELT, FAST> ta, tb;
-  SmallRegs<KIND, D> ra, rb;
-  ta.init(p, s, tile_of(a));
-  small_load_k<KIND, D, FAST>(p, s, ta, ra, n, h);
-  small_load_v<KIND, D, FAST>(p, s, ta, ra, n, h);
-  for (int u = a; u < b; u += 2) {
-    if (u + 1 < b) {
-      tb.init(p, s, tile_of(u + 1));
-      small_load_k<KIND, D, FAST>(p, s, tb, rb, n, h);
-      small_load_v<KIND, D, FAST>(p, s, tb, rb, n, h);
-    }
-    small_compute<KIND, D, FAST>(p, s, x, ta, ra, QFromLds<KIND, D>{qlds}, rm, bm_head, pos_min, left_max, st, lane);
-    if (u + 1 >= b) break;
-    if (u + 2 < b) {
-      ta.init(p, s, tile_of(u + 2));
-      small_load_k<KIND, D, FAST>(p, s, ta, ra, n, h);
-      small_load_v<KIND, D, FAST>(p, s, ta, ra, n, h);
-    }
-    small_compute<KIND, D, FAST>(p, s, x, tb, rb, QFromLds<KIND, D>{qlds}, rm, bm_head, pos_min, left_max, st, lane);
+  for (int u = a; u < b; ++u) {
+    // wave-uniform: keeps tile addressing in scalar registers
+    const int tile = __builtin_amdgcn_readfirstlane(p.bm ? (int)list[u - c0] : t_lo + u);
+    Tile<C::ELT, FAST> t;
+    SmallRegs<KIND, D> r;
+    t.init(p, s, tile);
+    small_load_k<KIND, D, FAST>(p, s, t, r, n, h);
+    small_load_v<KIND, D, FAST>(p, s, t, r, n, h);
+    small_compute<KIND, D, FAST>(p, s, x, t, r, QFromLds<KIND, D>{qlds}, rm, bm_head, pos_min, left_max, st, lane);
   }
 }
 
@@ -911,23 +907,18 @@ struct StreamRec {
   QBlock x;
   Tile<Cfg<KIND, D>::ELT, FAST> t;
   SmallRegs<KIND, D> r;
+  typename QKOpT<KIND>::T qB[Cfg<KIND, D>::KSQ];   // Q operands of the record's Q-block
 };
 
-// Where the prefetch stands: the Q-block of the last prepared unit, its unit
-// range [S, E), and a window of 64 page-table entries of its sequence held one
-// per lane, so that a tile's page costs a register read instead of a
-// dependent scalar memory load.  Q rows for a record that enters a new
-// Q-block are loaded into `qtmp` ahead of that record's K/V loads and moved to
-// the record's LDS slot at the next prepare, by when they have arrived
-// without waiting for any K/V load.
-template <int KIND, int D>
+// Where the stream stands: the Q-block of the current unit, its unit range
+// [S, E), and a window of 64 page-table entries of its sequence held one per
+// lane, so that a tile's page costs a register read instead of a dependent
+// scalar memory load.
 struct StreamCursor {
   int q, S, E, t_lo;
   QBlock x;
   int pbase;     // page-table index held by lane 0 of vpage
   int vpage;
-  int qpend;     // LDS slot waiting for qtmp, or -1
-  typename QKOpT<KIND>::T qtmp[Cfg<KIND, D>::KSQ];
 };
 
 template <int KIND, int D>
@@ -939,15 +930,9 @@ struct StashLayout {   // 8 pieces (2 per wave): m[16], l[16], acc[16][D] (raw),
 };
 
 template <int KIND, int D, bool FAST>
-__device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor<KIND, D>& c, StreamRec<KIND, D, FAST>& rec,
-                                               typename QKOpT<KIND>::T* qslots, int slot, int u, int n, int h,
-                                               int lane) {
+__device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c, StreamRec<KIND, D, FAST>& rec,
+                                               int u, int n, int h, int lane) {
   using C = Cfg<KIND, D>;
-  if (c.qpend >= 0) {                                    // Q rows of an earlier record: now in registers
-#pragma unroll
-    for (int ks = 0; ks < C::KSQ; ++ks) qslots[(c.qpend * C::KSQ + ks) * 64 + lane] = c.qtmp[ks];
-    c.qpend = -1;
-  }
   if (u >= c.E) {                                        // next Q-block (rare: scalar loads)
     int q = c.q;
     while (p.unit_prefix[q + 1] <= u) ++q;
@@ -961,14 +946,13 @@ __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor<KI
   }
   const QBlock& x = c.x;
   SeqCtx s{x.b, x.g, x.ctx, c.t_lo, p.bt + (int64_t)x.b * p.bt_stride};
-  if (rec.q != c.q) {                                    // the record enters a new Q-block: its Q rows first
+  if (rec.q != c.q) {                                    // a new Q-block: its Q rows
     // rows past the Q-block re-read row 0: finite scores that are never written
     const int r = n < x.rows ? n : 0;
     const int tok = x.q0 + x.t0 + r / p.G, head = x.g * p.G + r % p.G;
     const char* at = reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT;
     __builtin_assume(at != nullptr);
-    load_qk_row<KIND, D>(at, h, c.qtmp);
-    c.qpend = slot;
+    load_qk_row<KIND, D>(at, h, rec.qB);
     rec.q = c.q;
     rec.x = x;
     rec.t_lo = c.t_lo;
@@ -1006,8 +990,6 @@ __device__ void small_range(const KParams& p, int vw, int L, int a, int b, char*
   const int n = lane & 15, h = lane >> 4;
   float* stash = reinterpret_cast<float*>(smem);
   int* tags = reinterpret_cast<int*>(smem + SL::FLOATS * 4);
-  using QT = typename QKOpT<KIND>::T;
-  QT* qslots = reinterpret_cast<QT*>(smem + C::QSLOTS_OFF) + wave * 2 * C::KSQ * 64;
   if (lane < 2) tags[2 * wave + lane] = -1;
   const int cnt = b - a;
   const int wa = wave_uniform(a + (cnt * wave) / kWaves), wb = wave_uniform(a + (cnt * (wave + 1)) / kWaves);
@@ -1044,7 +1026,7 @@ __device__ void small_range(const KParams& p, int vw, int L, int a, int b, char*
           for (int md = 0; md < MD; ++md) stash[SL::ACC + (k * 16 + n) * D + out_dim<KIND, D>(h, j, md)] = st.acc[0][md][j];
       }
     };
-    auto consume = [&](const StreamRec<KIND, D, FAST>& rec, int slot) {
+    auto consume = [&](const StreamRec<KIND, D, FAST>& rec) {
       if (rec.q != cur_q) {
         if (cur_q >= 0) finish();
         cur_q = rec.q;
@@ -1058,8 +1040,8 @@ __device__ void small_range(const KParams& p, int vw, int L, int a, int b, char*
         left_max = p.window > 0 ? window_left(p, cx.pos_hi) : 0;
       }
       SeqCtx s{cx.b, cx.g, cx.ctx, rec.t_lo, p.bt + (int64_t)cx.b * p.bt_stride};
-      small_compute<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromLds<KIND, D>{qslots + slot * C::KSQ * 64}, rm, 0,
-                                   pos_min, left_max, st, lane);
+      small_compute<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromRegs<KIND, D>{rec.qB}, rm, 0, pos_min, left_max,
+                                   st, lane);
     };
     // the Q-block of the first unit: last q with unit_prefix[q] <= wa
     int lo = 0, hi = p.hdr[H_NQB] - 1;
@@ -1067,25 +1049,16 @@ __device__ void small_range(const KParams& p, int vw, int L, int a, int b, char*
       const int mid = (lo + hi + 1) >> 1;
       if (p.unit_prefix[mid] <= wa) lo = mid; else hi = mid - 1;
     }
-    StreamCursor<KIND, D> c;
+    StreamCursor c;
     c.q = wave_uniform(lo);
     c.E = -1;                                            // forces the Q-block load on the first unit
-    c.qpend = -1;
-    StreamRec<KIND, D, FAST> A, B;
-    A.q = -1;
-    B.q = -1;
-    // Every consume is preceded by a prepare of the other record (past the
-    // end it repeats the last unit, an L2 hit), so the loads in flight at
-    // each wait are the same on every path and the prepare also moves the
-    // consumed record's Q rows into LDS.
-    const int last = wb - 1;
-    stream_prepare<KIND, D, FAST>(p, c, A, qslots, 0, wa, n, h, lane);
-    for (int u = wa; u < wb; u += 2) {
-      stream_prepare<KIND, D, FAST>(p, c, B, qslots, 1, min(u + 1, last), n, h, lane);
-      consume(A, 0);
-      if (u + 1 >= wb) break;
-      stream_prepare<KIND, D, FAST>(p, c, A, qslots, 0, min(u + 2, last), n, h, lane);
-      consume(B, 1);
+    StreamRec<KIND, D, FAST> rec;
+    rec.q = -1;
+    // one tile in flight per wave; the second wave on each SIMD (two
+    // workgroups per compute unit) computes while this one waits
+    for (int u = wa; u < wb; ++u) {
+      stream_prepare<KIND, D, FAST>(p, c, rec, u, n, h, lane);
+      consume(rec);
     }
     finish();
   }
@@ -1436,14 +1409,12 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) sc[nb][mb] *= cs;
           if (!full) {
             ElemMask em;
             em.init(p, rm[nb], J0, nvalid, lmk);
             mask_scores(sc[nb], em, h);
           }
-          softmax_update<KIND, D, NB>(st, nb, sc[nb]);
+          softmax_update<KIND, D, NB>(st, nb, sc[nb], cs);
         }
         // O^T += V^T P^T
         if constexpr (KIND == KIND_F32) {
@@ -1517,9 +1488,21 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
 // ---------------------------------------------------------------------------
 // the persistent kernel
 // ---------------------------------------------------------------------------
+// The kernel's parameter block, read through the kernarg segment pointer (the
+// block is the kernel's only argument, at offset 0).  Each use site takes its
+// own opaque copy of the pointer, so a segment loads the parameters it needs
+// (scalar loads) where it starts, instead of the whole persistent kernel
+// holding every parameter in scalar registers from the first instruction.
+__device__ __forceinline__ const KParams& kparams() {
+  uint64_t v = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(v));
+  return *(const KParams*)(const __attribute__((address_space(4))) KParams*)v;
+}
+
 template <int KIND, int D, bool FAST>
-__global__ __launch_bounds__(kThreads, 1) void attention_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kernel(KParams) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  const KParams& p = kparams();
   const int U = p.hdr[H_U];
   const int L = p.hdr[H_L];
   const int n_workers = p.hdr[H_NWORKERS];
@@ -1554,7 +1537,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(KParams p) {
           ++qq;
         }
         run_end = wave_uniform(run_end);
-        small_range<KIND, D, FAST>(p, vw, L, a, run_end, smem);
+        small_range<KIND, D, FAST>(kparams(), vw, L, a, run_end, smem);
         a = run_end;
         while (q < n_qb && p.unit_prefix[q + 1] <= a) ++q;
         continue;
@@ -1563,8 +1546,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(KParams p) {
       qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, t_lo, t_hi);
       const bool final_out = p.n_splits[q] == 1;
       const int slot = final_out ? 0 : p.slot_base[q] + (vw - S / L);
-      if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(p, x, t_lo, t_hi, u0, u1, final_out, slot, smem);
-      else large_segment<KIND, D, FAST>(p, x, t_lo, t_hi, u0, u1, final_out, slot, smem);
+      if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(kparams(), x, t_lo, t_hi, u0, u1, final_out, slot, smem);
+      else large_segment<KIND, D, FAST>(kparams(), x, t_lo, t_hi, u0, u1, final_out, slot, smem);
       a = S + u1;
       ++q;
     }

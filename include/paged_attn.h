@@ -81,7 +81,8 @@ typedef enum pa_scale_mode {
 } pa_scale_mode;
 
 /* FP8 dequantisation scales (device pointers, so a call never reads them on
- * the host and stays capturable in a HIP graph).  Value = e4m3(x) * scale.
+ * the host and stays capturable in a HIP graph).  Value = e4m3(x) * scale;
+ * every scale must be finite and > 0.
  * Required when Q/K/V are PA_F8E4M3, ignored otherwise. */
 typedef struct pa_scales {
   int32_t mode;             /* pa_scale_mode */
@@ -102,14 +103,14 @@ typedef struct pa_params {
   int32_t block_table_stride;   /* elements between rows of block_table (>= max_pages_per_seq) */
   int32_t total_q;              /* query tokens = query_start_loc[B] */
   /* scores and masking */
-  float softmax_scale;          /* multiplies Q.K (fp32, used as given) */
+  float softmax_scale;          /* multiplies Q.K (fp32, used as given); finite and > 0 */
   int32_t causal;               /* 1: key j visible only if j <= pos (bottom-right aligned) */
   int32_t window;               /* > 0: sliding window of this many keys ending at pos */
   int32_t window_expand_to_chunk; /* 1: window start rounded down to a multiple of landmark_chunk */
   int32_t landmark_chunk;       /* C > 0: hide keys with (j + 1) % C == 0 */
   int32_t block_mask_tile;      /* tile edge of block_mask in tokens; multiple of 64; 0 = 128 */
   /* scheduling */
-  int32_t num_workers;          /* P persistent workgroups; 0 = one per compute unit */
+  int32_t num_workers;          /* P persistent workgroups; 0 = two per compute unit */
   int32_t split_min_units;      /* L_min: fewest 64-key units a worker is given; 0 = 8 */
   int32_t force_split_units;    /* > 0: every worker gets exactly this many units (testing) */
   int32_t max_partial_slots;    /* capacity for split partial outputs; 0 = 2 * P */

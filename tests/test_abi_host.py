@@ -59,7 +59,9 @@ def test_workspace_size_closed_form():
 
 @pytest.mark.parametrize("bad", [dict(head_dim=96), dict(num_kv_heads=5), dict(page_size=48),
                                  dict(num_q_heads=24, num_kv_heads=8), dict(block_mask_tile=100),
-                                 dict(num_seqs=0), dict(max_pages_per_seq=0), dict(window=-1)])
+                                 dict(num_seqs=0), dict(max_pages_per_seq=0), dict(window=-1),
+                                 dict(softmax_scale=0.0), dict(softmax_scale=-0.1),
+                                 dict(softmax_scale=float("inf")), dict(softmax_scale=float("nan"))])
 def test_bad_params_rejected(bad):
     p = _params(**bad)
     n = ctypes.c_size_t()
