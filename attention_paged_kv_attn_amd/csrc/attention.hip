@@ -128,6 +128,57 @@ __device__ __forceinline__ int page_of(const KParams& p, const SeqCtx& s, int ke
   return page;
 }
 
+// The kernel's parameter block, read through the kernarg segment pointer (the
+// block is the kernel's only argument, at offset 0).  Every use site takes its
+// own opaque copy of the pointer, so a segment loads the parameters it needs
+// (scalar loads) where it starts, instead of the whole persistent kernel
+// holding every parameter in scalar registers from the first instruction.  The
+// pointer itself exists only in the kernel (a called function would see null),
+// so the kernel reads it once and hands the value down (kparams_at).
+// A 64-bit value made wave-uniform.  The builtin returns a signed int, so each
+// half goes through uint32_t before widening (no sign extension).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Segment functions are inlined into the kernel: measured faster than
+// separate calls (whose callee-saved registers and call boundaries cost more
+// than the separate register allocation gains).
+#ifndef PA_SEGMENT_FN
+#define PA_SEGMENT_FN __attribute__((always_inline))
+#endif
+
+__device__ __forceinline__ uint64_t kparams_addr() {
+  return reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+}
+__device__ __forceinline__ const KParams& kparams_at(uint64_t v) {
+  v = uniform_u64(v);
+  asm volatile("" : "+s"(v));
+  return *(const KParams*)(const __attribute__((address_space(4))) KParams*)v;
+}
+
+// Reductions over the four lanes n, n + 16, n + 32, n + 48 that share a query
+// row, with the lane-swap instructions (no LDS round trip): the swap of a
+// register with itself hands each lane both halves of the exchanged pair.
+__device__ __forceinline__ float row_max4(float x) {
+  const unsigned u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);      // lanes l & ~16, l | 16
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);      // lanes l & ~32, l | 32
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  const unsigned u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Values the whole wave shares, made explicit for the compiler (so addressing
 // stays in scalar registers and buffer resources need no per-lane loop).
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -313,7 +364,9 @@ struct ElemMask {
     if (p.causal) hi = min(hi, r.pos - J0 + 1);
     lo = p.window > 0 ? max(0, r.left - J0) : 0;
     span = (r.bit && hi > lo) ? (unsigned)(hi - lo) : 0u;
-    lm = lmk;
+    // re-read as a wave-uniform value here, where a tile needs masking, so
+    // that the per-element landmark tests are not hoisted into every tile
+    lm = uniform_u64(lmk);
   }
   __device__ __forceinline__ bool ok(int o) const {
     bool v = (unsigned)(o - lo) < span;
@@ -342,11 +395,13 @@ struct WaveState {
   f32x4 acc[NB][Cfg<KIND, D>::MD];
   float m2[NB];       // running max of log2-domain scores of this lane's row
   float lsum[NB];     // this lane's share of the running sum (reduced at the end)
+  f32x4 lacc[NB];     // or: the row's whole running sum, accumulated by MFMA
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m2[nb] = kNegInf;
       lsum[nb] = 0.f;
+      lacc[nb] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int md = 0; md < Cfg<KIND, D>::MD; ++md) acc[nb][md] = f32x4{0, 0, 0, 0};
     }
@@ -361,21 +416,21 @@ struct WaveState {
 // below 2^kRescaleSlack (exact in the result: l and O use the same m).
 constexpr float kRescaleSlack = 8.f;
 
-template <int KIND, int D, int NB>
+template <int KIND, int D, int NB, bool VSUM = true>
 __device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int nb, f32x4 (&s)[4], float cs) {
   float mx = kNegInf;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mb][j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = row_max4(mx);
   const float m_cand = mx == kNegInf ? kNegInf : mx * cs;
   const bool grow = m_cand > st.m2[nb] + kRescaleSlack;
   if (__ballot(grow) != 0) {                            // wave-uniform, rare after the first tiles
     const float m_new = grow ? m_cand : st.m2[nb];
     const float alpha = st.m2[nb] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st.m2[nb] - m_new);
-    st.lsum[nb] *= alpha;
+    if constexpr (VSUM) st.lsum[nb] *= alpha;
+    else st.lacc[nb] *= alpha;
 #pragma unroll
     for (int md = 0; md < Cfg<KIND, D>::MD; ++md) st.acc[nb][md] *= alpha;
     st.m2[nb] = m_new;
@@ -388,9 +443,15 @@ __device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int n
     for (int j = 0; j < 4; ++j) {
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][j], cs, nmref));
       s[mb][j] = e;
-      sum += e;
+      if constexpr (VSUM) sum += e;
     }
-  st.lsum[nb] += sum;
+  if constexpr (VSUM) st.lsum[nb] += sum;
+}
+
+// An all-ones bf16 A operand: MFMA against a P^T operand yields the P row sums
+// (the same bf16 probabilities PV uses) replicated over the output rows.
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 }
 
 // P^T operand (bf16) of PV K-step ks2: slot t = key 32 ks2 + 16 (t / 4) + 4 h + t % 4.
@@ -785,8 +846,10 @@ __device__ __forceinline__ void small_run(const KParams& p, const SeqCtx& s, con
 }
 
 template <int KIND, int D, bool FAST>
-__device__ void small_segment(const KParams& p, const QBlock& x, int t_lo, int t_hi, int u0, int u1,
-                              bool final_out, int slot, char* smem) {
+__device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_lo, int t_hi, int u0,
+                                                       int u1, bool final_out, int slot) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const KParams& p = kparams_at(pk);
   using C = Cfg<KIND, D>;
   constexpr int MD = C::MD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -831,8 +894,7 @@ __device__ void small_segment(const KParams& p, const QBlock& x, int t_lo, int t
 
   // merge the four waves' states through LDS: m, l per row; acc per row x dims
   float l = st.lsum[0];
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = row_sum4(l);
   float* mrg = reinterpret_cast<float*>(smem);
   float* ms = mrg;                                     // [wave][16]
   float* ls = mrg + kWaves * 16;                       // [wave][16]
@@ -982,7 +1044,9 @@ __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c
 }
 
 template <int KIND, int D, bool FAST>
-__device__ void small_range(const KParams& p, int vw, int L, int a, int b, char* smem) {
+__device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int b) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const KParams& p = kparams_at(pk);
   using C = Cfg<KIND, D>;
   using SL = StashLayout<KIND, D>;
   constexpr int MD = C::MD;
@@ -1004,8 +1068,7 @@ __device__ void small_range(const KParams& p, int vw, int L, int a, int b, char*
     st.init();
     auto finish = [&]() {
       float l = st.lsum[0];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      l = row_sum4(l);
       const int S = p.unit_prefix[cur_q], E = p.unit_prefix[cur_q + 1];
       if (S >= wa && E <= wb) {                          // whole Q-block in this quarter: final output
         if (n < cx.rows) {
@@ -1237,30 +1300,69 @@ struct Stage {
 // chunk q stored in slot q ^ 2 (r % 8), so the transpose reads of a V^T
 // operand (16 rows x 32 bytes) spread over all LDS banks.
 struct DirectStage {
-  __device__ __forceinline__ static void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
-    Tile<2, true> t;
-    t.init(p, s, tile);
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Per segment: the sequence's K/V bases for kv head g, byte strides, and a
+  // 64-entry window of its page table held one entry per lane (a tile's page
+  // is then a register read, not a dependent scalar load).
+  const char* kbase;
+  const char* vbase;
+  uint64_t ksp, vsp;          // bytes between pages
+  uint32_t kss, vss;          // bytes between slots
+  const int32_t* bt_row;
+  int pbase, vpage;
+  // per lane: constant parts of the load offsets
+  uint32_t k_col, v_col;      // byte column within a row
+  int k_row0, v_row0;         // row of load i = 0 (K: + 16 i, V: + 16 i)
+
+  __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s) {
+    kbase = wave_uniform(reinterpret_cast<const char*>(p.k) + (int64_t)s.g * p.k_sh * 2);
+    vbase = wave_uniform(reinterpret_cast<const char*>(p.v) + (int64_t)s.g * p.v_sh * 2);
+    ksp = (uint64_t)p.k_sp * 2;
+    vsp = (uint64_t)p.v_sp * 2;
+    kss = (uint32_t)(p.k_ss * 2);
+    vss = (uint32_t)(p.v_ss * 2);
+    bt_row = s.bt_row;
+    pbase = -(1 << 30);
+    vpage = 0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, hh = lane >> 4;
-    const bool full = t.nvalid == kUnitKeys;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int mk = 4 * i + wave, mb = mk >> 2, ks = mk & 3;
-      const uint32_t voff = full ? (uint32_t)m * t.kss + 16 * hh
-                                 : (uint32_t)min(16 * mb + m, t.nvalid - 1) * t.kss + 16 * hh;
-      const uint32_t soff = full ? (uint32_t)(16 * mb) * t.kss + 64 * ks : 64u * ks;
-      gload16_lds(t.kb, kbuf + 1024 * mk, voff, soff);
+    k_row0 = m;
+    k_col = 64u * wave + 16u * hh;                      // K-step ks = wave, dims 32 ks + 8 hh
+    const int rl = lane >> 4, sl = lane & 15;
+    v_row0 = 4 * wave + rl;                             // row 16 i + 4 wave + rl
+    v_col = 16u * (sl ^ (2 * (v_row0 & 7)));             // swizzled 16-byte column (row & 7 is i-invariant)
+  }
+
+  __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
+    const int idx = J0 >> p.page_shift;
+    if ((unsigned)(idx - pbase) >= 64u) {                // refill the window (rare)
+      pbase = idx;
+      int v = bt_row[min(idx + (int)(threadIdx.x & 63), p.max_pages - 1)];
+      asm volatile("" : "+v"(v));                       // complete the load here
+      vpage = v;
     }
-    const int sl = lane & 15, rl = lane >> 4;
+    int page = idx < p.max_pages ? __builtin_amdgcn_readlane(vpage, idx - pbase) : -1;
+    if ((unsigned)page >= (unsigned)p.num_pages) {
+      p.hdr[H_ERROR] = E_PAGE;
+      page = 0;
+    }
+    return page;
+  }
+
+  // K in MFMA-operand order at kbuf + 1024 (4 mb + ks); V row-major, 16-byte
+  // columns swizzled by row, at vbuf.  Rows past the sequence end re-read its
+  // last key (finite values; their scores are masked).
+  __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
+    const int J0 = tile * kUnitKeys;
+    const int page = page_of_tile(p, J0);
+    const uint32_t slot = (uint32_t)(J0 & (p.page_size - 1));
+    const char* kb = wave_uniform(kbase + page * ksp + slot * kss);
+    const char* vb = wave_uniform(vbase + page * vsp + slot * vss);
+    const int lim = min(kUnitKeys, s.ctx - J0) - 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r4 = 4 * i + wave, row = 4 * r4 + rl;
-      const int q = sl ^ (2 * (row & 7));
-      const uint32_t voff = full ? (uint32_t)rl * t.vss + 16 * q
-                                 : (uint32_t)min(row, t.nvalid - 1) * t.vss + 16 * q;
-      const uint32_t soff = full ? (uint32_t)(4 * r4) * t.vss : 0u;
-      gload16_lds(t.vb, vbuf + 1024 * r4, voff, soff);
+      gload16_lds(kb, kbuf + 1024 * (4 * i + wave), (uint32_t)min(k_row0 + 16 * i, lim) * kss + k_col, 0u);
+      gload16_lds(vb, vbuf + 1024 * (4 * i + wave), (uint32_t)min(v_row0 + 16 * i, lim) * vss + v_col, 0u);
     }
   }
 };
@@ -1274,28 +1376,39 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // (+16 for slots 4..7), dims 16 md + 4 c; the read hands lane i the dim
 // 16 md + i of those 4 rows.  `base0` is the lane's byte offset with md = 0
 // (row part + swizzle bits), so the md offset is an XOR on bits 5..7.
-__device__ __forceinline__ bf16x8 v_operand_tr(const char* smem, uint32_t base0, int ks2, int md) {
-  const uint32_t a = (base0 + ks2 * 8192u) ^ (32u * md);
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(smem + a));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(smem + a + 4096));
+// `trx` = the lane's offset with the md XOR applied (below 4096, so adding a
+// buffer offset that is a multiple of 4096 commutes with the XOR and folds
+// into the instruction's immediate offset).
+__device__ __forceinline__ bf16x8 v_operand_tr(const char* smem, uint32_t trx, uint32_t off) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(smem + trx + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(smem + trx + off + 4096));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
 template <int KIND, int D, bool FAST>
-__device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t_hi, int u0, int u1,
-                              bool final_out, int slot, char* smem) {
+__device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_lo, int t_hi, int u0,
+                                                       int u1, bool final_out, int slot) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const KParams& p = kparams_at(pk);
   using C = Cfg<KIND, D>;
   constexpr int MD = C::MD;
   constexpr int NB = 2;
   constexpr bool DIRECT = KIND == KIND_BF16 && D == 128 && FAST;
+  // Row sums of P stay on the VALU in fp32: an MFMA sum of the bf16 P operand
+  // carries its rounding (up to 2^-9 on the largest term, which under the lazy
+  // rescale is no longer exactly 1) straight into the LSE.
+  constexpr bool MSUM = false;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, h = lane >> 4;
   short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
   SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
-  // transpose-read lane offset (see v_operand_tr), relative to a V buffer
+  // transpose-read lane offsets (see v_operand_tr), relative to a V buffer
   const int trk = n >> 2, trc = n & 3;
   const uint32_t tr_lane = (uint32_t)(4 * h + trk) * 256u + 32u * ((4 * h + trk) & 7) + 16u * (trc >> 1) + 8u * (trc & 1);
+  uint32_t trx[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) trx[md] = tr_lane ^ (32u * md);
 
   // this lane's two rows
   typename QKOpT<KIND>::T qB[NB][C::KSQ];
@@ -1329,6 +1442,8 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
   WaveState<KIND, D, NB> st;
   st.init();
   Stage<KIND, D, FAST> stg;
+  DirectStage ds;
+  if constexpr (DIRECT) ds.init(p, s);
 
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
     const int cn = min(kMaskListCap, u1 - c0);
@@ -1337,22 +1452,24 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
     return __builtin_amdgcn_readfirstlane(p.bm ? (int)list[u - c0] : t_lo + u);
   };
     if constexpr (DIRECT) {
-      DirectStage::load(p, s, tile_of(c0), smem, smem + C::K_TILE);
+      ds.load(p, s, tile_of(c0), smem, smem + C::K_TILE);
       wait_vmem();
     } else {
       stg.load(p, s, tile_of(c0));
       stg.store(smem, smem + C::K_TILE);
     }
     __syncthreads();
-    for (int u = c0; u < c0 + cn; ++u) {
-      const int buf = (u - c0) & 1;
+    // one tile; BUF (a compile-time 0 / 1) selects the stage it reads, so every
+    // LDS address is a lane register plus an immediate offset
+    auto step = [&](int u, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
       char* kbuf = smem + buf * C::STAGE;
       char* vbuf = kbuf + C::K_TILE;
       const bool more = u + 1 < c0 + cn;
       if (more) {
         if constexpr (DIRECT) {
           char* nk = smem + (buf ^ 1) * C::STAGE;
-          DirectStage::load(p, s, tile_of(u + 1), nk, nk + C::K_TILE);
+          ds.load(p, s, tile_of(u + 1), nk, nk + C::K_TILE);
         } else {
           stg.load(p, s, tile_of(u + 1));
         }
@@ -1414,7 +1531,7 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
             em.init(p, rm[nb], J0, nvalid, lmk);
             mask_scores(sc[nb], em, h);
           }
-          softmax_update<KIND, D, NB>(st, nb, sc[nb], cs);
+          softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], cs);
         }
         // O^T += V^T P^T
         if constexpr (KIND == KIND_F32) {
@@ -1432,15 +1549,18 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
                     st.acc[nb][4 * gd + i] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], sc[nb][mb][j], st.acc[nb][4 * gd + i], 0, 0, 0);
               }
         } else if constexpr (DIRECT) {
-          const uint32_t base0 = (uint32_t)(vbuf - smem) + tr_lane;
 #pragma unroll
           for (int ks2 = 0; ks2 < 2; ++ks2) {
             bf16x8 pb[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) pb[nb] = p_operand(sc[nb], ks2, vsc);
+            if constexpr (MSUM) {
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) st.lacc[nb] = mfma_pv(ones_bf16x8(), pb[nb], st.lacc[nb]);
+            }
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
-              const bf16x8 va = v_operand_tr(smem, base0, ks2, md);
+              const bf16x8 va = v_operand_tr(smem, trx[md], (uint32_t)(buf * C::STAGE + C::K_TILE + ks2 * 8192));
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) st.acc[nb][md] = mfma_pv(va, pb[nb], st.acc[nb][md]);
             }
@@ -1451,6 +1571,10 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
             bf16x8 pb[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) pb[nb] = p_operand(sc[nb], ks2, vsc);
+            if constexpr (MSUM) {
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) st.lacc[nb] = mfma_pv(ones_bf16x8(), pb[nb], st.lacc[nb]);
+            }
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
               const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vbuf + ((ks2 * MD + md) * 64 + lane) * 16));
@@ -1468,15 +1592,17 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
         stg.store(nk, nk + C::K_TILE);
       }
       __syncthreads();
+    };
+    for (int u = c0; u < c0 + cn; u += 2) {
+      step(u, std::integral_constant<int, 0>{});
+      if (u + 1 < c0 + cn) step(u + 1, std::integral_constant<int, 1>{});
     }
   }
 
   // epilogue: per lane row, reduce l over the four lane groups and write
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    float l = st.lsum[nb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = MSUM ? st.lacc[nb][0] : row_sum4(st.lsum[nb]);
     if (!rok[nb]) continue;
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
@@ -1488,21 +1614,12 @@ __device__ void large_segment(const KParams& p, const QBlock& x, int t_lo, int t
 // ---------------------------------------------------------------------------
 // the persistent kernel
 // ---------------------------------------------------------------------------
-// The kernel's parameter block, read through the kernarg segment pointer (the
-// block is the kernel's only argument, at offset 0).  Each use site takes its
-// own opaque copy of the pointer, so a segment loads the parameters it needs
-// (scalar loads) where it starts, instead of the whole persistent kernel
-// holding every parameter in scalar registers from the first instruction.
-__device__ __forceinline__ const KParams& kparams() {
-  uint64_t v = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
-  asm volatile("" : "+s"(v));
-  return *(const KParams*)(const __attribute__((address_space(4))) KParams*)v;
-}
 
 template <int KIND, int D, bool FAST>
 __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kernel(KParams) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const KParams& p = kparams();
+  const uint64_t pk = kparams_addr();
+  const KParams& p = kparams_at(pk);
   const int U = p.hdr[H_U];
   const int L = p.hdr[H_L];
   const int n_workers = p.hdr[H_NWORKERS];
@@ -1537,7 +1654,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kerne
           ++qq;
         }
         run_end = wave_uniform(run_end);
-        small_range<KIND, D, FAST>(kparams(), vw, L, a, run_end, smem);
+        small_range<KIND, D, FAST>(pk, vw, L, a, run_end);
         a = run_end;
         while (q < n_qb && p.unit_prefix[q + 1] <= a) ++q;
         continue;
@@ -1546,8 +1663,8 @@ __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kerne
       qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, t_lo, t_hi);
       const bool final_out = p.n_splits[q] == 1;
       const int slot = final_out ? 0 : p.slot_base[q] + (vw - S / L);
-      if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(kparams(), x, t_lo, t_hi, u0, u1, final_out, slot, smem);
-      else large_segment<KIND, D, FAST>(kparams(), x, t_lo, t_hi, u0, u1, final_out, slot, smem);
+      if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
+      else large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
       a = S + u1;
       ++q;
     }
