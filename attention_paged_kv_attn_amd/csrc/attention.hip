@@ -354,37 +354,53 @@ __device__ __forceinline__ uint64_t landmark_bits(const KParams& p, int J0) {
   return m;
 }
 
-// Visible key offsets of one row inside a tile: lo <= o < lo + span, minus landmarks.
+// The landmark flags of a lane's 16 scores (bit 4 mb + j <-> key offset
+// 16 mb + 4 h + j) from a tile's 64-bit landmark bitmap.
+__device__ __forceinline__ uint32_t lane_bits16(uint64_t bits64, int h) {
+  const uint64_t x = bits64 >> (4 * h);
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  return (lo & 0xFu) | ((lo >> 12) & 0xF0u) | ((hi & 0xFu) << 8) | ((hi >> 4) & 0xF000u);
+}
+
+// Visible key offsets of one row inside a tile: lo <= o < lo + span, minus the
+// landmarks flagged in l16 (the lane's 16 scores).
 struct ElemMask {
   int lo;
   unsigned span;
-  uint64_t lm;
-  __device__ __forceinline__ void init(const KParams& p, const RowMask& r, int J0, int nvalid, uint64_t lmk) {
+  uint32_t l16;
+  __device__ __forceinline__ void init(const KParams& p, const RowMask& r, int J0, int nvalid, uint64_t lmk, int h) {
     int hi = nvalid;
     if (p.causal) hi = min(hi, r.pos - J0 + 1);
     lo = p.window > 0 ? max(0, r.left - J0) : 0;
     span = (r.bit && hi > lo) ? (unsigned)(hi - lo) : 0u;
-    // re-read as a wave-uniform value here, where a tile needs masking, so
-    // that the per-element landmark tests are not hoisted into every tile
-    lm = uniform_u64(lmk);
-  }
-  __device__ __forceinline__ bool ok(int o) const {
-    bool v = (unsigned)(o - lo) < span;
-    if (lm) v = v && !((lm >> o) & 1ull);
-    return v;
+    l16 = lmk ? lane_bits16(lmk, h) : 0u;
   }
 };
 
-// The tile needs no per-element mask for any row with positions in [pos_min, ...]
-// and window starts <= left_max.
-__device__ __forceinline__ bool unit_is_full(const KParams& p, int J0, int nvalid, int pos_min,
-                                             int left_max, uint64_t lmk) {
+// The tile needs no causal, window, length or block-mask test for any row with
+// positions in [pos_min, ...] and window starts <= left_max (landmarks aside).
+__device__ __forceinline__ bool unit_is_full(const KParams& p, int J0, int nvalid, int pos_min, int left_max) {
   if (nvalid < kUnitKeys) return false;
   if (p.causal && J0 + kUnitKeys - 1 > pos_min) return false;
   if (p.window > 0 && J0 < left_max) return false;
-  if (lmk) return false;
   if (p.bm) return false;
   return true;
+}
+
+// Landmark keys only (the tile is otherwise fully visible): the scores whose
+// slot holds a landmark for some lane group are visited, the others skipped
+// by a wave-uniform test.
+__device__ __forceinline__ void mask_landmarks(f32x4 (&sc)[4], uint64_t lmk, int h) {
+  uint32_t any = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) any |= lane_bits16(lmk, g);
+  any = __builtin_amdgcn_readfirstlane(any);
+  const uint32_t l16 = lane_bits16(lmk, h);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((any >> (4 * mb + j)) & 1u) sc[mb][j] = ((l16 >> (4 * mb + j)) & 1u) ? kNegInf : sc[mb][j];
 }
 
 // ---------------------------------------------------------------------------
@@ -727,26 +743,16 @@ __device__ __forceinline__ void small_load_v(const KParams& p, const SeqCtx& s, 
   }
 }
 
-// Apply the per-element mask of one row-block (lane's row) to log2-domain scores.
+// Apply the per-element mask of one row-block (lane's row) to the scores.
 __device__ __forceinline__ void mask_scores(f32x4 (&sc)[4], const ElemMask& em, int h) {
-  if (em.lm) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = 16 * mb + 4 * h + j;
-        const bool ok = ((unsigned)(o - em.lo) < em.span) && !((em.lm >> o) & 1ull);
-        sc[mb][j] = ok ? sc[mb][j] : kNegInf;
-      }
-  } else {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = 16 * mb + 4 * h + j;
-        sc[mb][j] = ((unsigned)(o - em.lo) < em.span) ? sc[mb][j] : kNegInf;
-      }
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int o = 16 * mb + 4 * h + j;
+      const bool ok = ((unsigned)(o - em.lo) < em.span) && !((em.l16 >> (4 * mb + j)) & 1u);
+      sc[mb][j] = ok ? sc[mb][j] : kNegInf;
+    }
 }
 
 // Q operands of a small Q-block, staged in LDS (element ks * 64 + lane holds
@@ -791,13 +797,15 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
     for (int mb = 0; mb < 4; ++mb) sc[mb] = mfma_qk(r.kA[mb][ks], qb, sc[mb]);
   }
   const uint64_t lmk = landmark_bits(p, J0);
-  const bool full = unit_is_full(p, J0, tc.nvalid, pos_min, left_max, lmk);
+  const bool full = unit_is_full(p, J0, tc.nvalid, pos_min, left_max);
   float cs = p.sm_log2;
   if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
   if (!full) {
     ElemMask em;
-    em.init(p, rm, J0, tc.nvalid, lmk);
+    em.init(p, rm, J0, tc.nvalid, lmk, h);
     mask_scores(sc, em, h);
+  } else if (lmk) {
+    mask_landmarks(sc, lmk, h);
   }
   softmax_update<KIND, D, 1>(st, 0, sc, cs);
   // O^T += V^T P^T
@@ -1492,7 +1500,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         }
         const int nvalid = min(kUnitKeys, x.ctx - J0);
         const uint64_t lmk = landmark_bits(p, J0);
-        const bool full = unit_is_full(p, J0, nvalid, pos_min, left_max, lmk);
+        const bool full = unit_is_full(p, J0, nvalid, pos_min, left_max);
         // S^T = K Q^T
         f32x4 sc[NB][4];
 #pragma unroll
@@ -1528,8 +1536,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         for (int nb = 0; nb < NB; ++nb) {
           if (!full) {
             ElemMask em;
-            em.init(p, rm[nb], J0, nvalid, lmk);
+            em.init(p, rm[nb], J0, nvalid, lmk, h);
             mask_scores(sc[nb], em, h);
+          } else if (lmk) {
+            mask_landmarks(sc[nb], lmk, h);
           }
           softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], cs);
         }
