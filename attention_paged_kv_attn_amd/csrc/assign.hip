@@ -14,6 +14,12 @@
 namespace pa {
 
 constexpr int kAssignThreads = 1024;
+constexpr int kAssignMaskLds = 64 * 1024;   // block masks up to this many bytes are staged in LDS
+
+// Bytes of the block mask as a dense [B, H_m, n_q_tiles, n_k_tiles] array.
+__host__ __device__ inline long long mask_elems(const KParams& p) {
+  return p.bm == nullptr ? 0 : (long long)p.B * p.bm_heads * p.bm_nq * p.bm_nk;
+}
 
 // Exclusive prefix sum over the workgroup; *total gets the sum.  `sh` holds
 // kAssignThreads / 64 + 1 ints of LDS.
@@ -47,8 +53,24 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh) 
 __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
   __shared__ int sh[kAssignThreads / 64 + 1];
   __shared__ int err;
+  extern __shared__ uint8_t mask_lds[];
   const int tid = threadIdx.x;
   if (tid == 0) err = E_NONE;
+  // A small block mask is copied into LDS first (independent byte loads from
+  // every thread) so that the per-Q-block tile counts below read LDS instead of
+  // issuing one dependent global load per tile.
+  const long long melems = mask_elems(p);
+  const bool staged = melems > 0 && melems <= kAssignMaskLds;
+  if (staged) {
+    for (int i = tid; i < (int)melems; i += kAssignThreads) {
+      int r = i;
+      const int kt = r % p.bm_nk; r /= p.bm_nk;
+      const int qt = r % p.bm_nq; r /= p.bm_nq;
+      const int hm = r % p.bm_heads;
+      const int b = r / p.bm_heads;
+      mask_lds[i] = p.bm[b * p.bm_sb + hm * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+    }
+  }
   __syncthreads();
 
   // 0. metadata checks: qsl is a non-decreasing prefix ending at total_q, q_len <= seq_len
@@ -109,7 +131,20 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
       if (p.bm == nullptr) {
         n = t_hi - t_lo + 1;
       } else {
-        for (int tl = t_lo; tl <= t_hi; ++tl) n += mask_union(p, b, g, pos_lo, pos_hi, tl) ? 1 : 0;
+        // walk the mask columns kt (T = block_mask_tile keys = upt 64-key
+        // tiles): a set column adds its tiles that lie in [t_lo, t_hi]
+        const int upt = p.bm_tile / kUnitKeys;
+        const int kt_lo = t_lo / upt, kt_hi = min(t_hi / upt, p.bm_nk - 1);
+        const int qt0 = pos_lo / p.bm_tile, qt1 = min(pos_hi / p.bm_tile, p.bm_nq - 1);
+        const int h0 = p.bm_heads == 1 ? 0 : g * p.G, h1 = p.bm_heads == 1 ? 1 : (g + 1) * p.G;
+        for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+          bool on = false;
+          for (int hm = h0; hm < h1 && !on; ++hm)
+            for (int qt = qt0; qt <= qt1 && !on; ++qt)
+              on = staged ? mask_lds[(((long long)b * p.bm_heads + hm) * p.bm_nq + qt) * p.bm_nk + kt] != 0
+                          : p.bm[b * p.bm_sb + hm * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+          if (on) n += min(t_hi, kt * upt + upt - 1) - max(t_lo, kt * upt) + 1;
+        }
       }
     }
     p.unit_prefix[q + 1] = n;
@@ -167,7 +202,16 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
 }
 
 hipError_t launch_assign(const KParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), 0, stream, p);
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&assign_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kAssignMaskLds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const long long me = mask_elems(p);
+  const int lds = (me > 0 && me <= kAssignMaskLds) ? (int)((me + 15) & ~15LL) : 0;
+  hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), lds, stream, p);
   return hipGetLastError();
 }
 

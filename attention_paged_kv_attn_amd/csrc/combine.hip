@@ -20,10 +20,51 @@ __device__ __forceinline__ unsigned pack_bf16x2_c(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+// One split merged into a running (m, z, o) state (natural-log domain LSEs):
+// m = running max, z = sum of e^(LSE_s - m), o = sum of e^(LSE_s - m) O_s.
+struct MergeState {
+  float m, z, o[8];
+};
+
+__device__ __forceinline__ void merge_part(MergeState& st, float ls, const float* src) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  if (!(ls > -__builtin_huge_valf())) return;          // an empty part weighs nothing
+  const f32x4c a = *reinterpret_cast<const f32x4c*>(src);
+  const f32x4c b = *reinterpret_cast<const f32x4c*>(src + 4);
+  const float m_new = fmaxf(st.m, ls);
+  const float alpha = st.m == -__builtin_huge_valf() ? 0.f : exp2f((st.m - m_new) * kLog2e);
+  const float w = exp2f((ls - m_new) * kLog2e);
+  st.z = st.z * alpha + w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    st.o[k] = st.o[k] * alpha + w * a[k];
+    st.o[4 + k] = st.o[4 + k] * alpha + w * b[k];
+  }
+  st.m = m_new;
+}
+
+__device__ __forceinline__ void merge_state(MergeState& st, const MergeState& other) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  if (other.m == -__builtin_huge_valf()) return;
+  const float m_new = fmaxf(st.m, other.m);
+  const float a = st.m == -__builtin_huge_valf() ? 0.f : exp2f((st.m - m_new) * kLog2e);
+  const float b = exp2f((other.m - m_new) * kLog2e);
+  st.z = st.z * a + other.z * b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * a + other.o[k] * b;
+  st.m = m_new;
+}
+
+// A workgroup per split Q-block.  Thread (group, row, 8 dims): when a
+// Q-block's rows need fewer than 256 threads, the spare threads form groups
+// that take every groups-th split, and the groups' states are merged through
+// LDS, so that a Q-block cut into many splits (a long decode) is read with
+// many loads in flight instead of one chain per row.
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(KParams p) {
-  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  constexpr float kLn2 = 0.6931471805599453f;
   const float ninf = -__builtin_huge_valf();
+  __shared__ MergeState red[256];
   const int n_combine = p.hdr[H_NCOMBINE];
   constexpr int TPR = D / 8;
   for (int i = blockIdx.x; i < n_combine; i += gridDim.x) {
@@ -31,41 +72,51 @@ __global__ __launch_bounds__(256) void combine_kernel(KParams p) {
     const QBlock x = load_qblock(p, q);
     const int ns = p.n_splits[q];
     const int sb = p.slot_base[q];
-    for (int idx = threadIdx.x; idx < x.rows * TPR; idx += blockDim.x) {
+    const int per = x.rows * TPR;                      // threads one pass over the rows needs
+    const int groups = per >= 256 ? 1 : 256 / per;
+    for (int base = 0; base < per; base += 256) {
+      const int t = threadIdx.x;
+      const int grp = groups > 1 ? t / per : 0;
+      const int idx = groups > 1 ? t % per : base + t;
+      const bool live = grp < groups && idx < per;
       const int row = idx / TPR, d0 = (idx % TPR) * 8;
-      float M = ninf;
-      for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, p.part_lse[(sb + sp) * kLargeRows + row]);
-      float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      float lse = ninf;
-      if (M != ninf) {
-        float z = 0.f;
-        for (int sp = 0; sp < ns; ++sp) z += exp2f((p.part_lse[(sb + sp) * kLargeRows + row] - M) * kLog2e);
-        lse = M + log2f(z) * kLn2;
-        for (int sp = 0; sp < ns; ++sp) {
-          const float ls = p.part_lse[(sb + sp) * kLargeRows + row];
-          if (ls == ninf) continue;
-          const float w = exp2f((ls - lse) * kLog2e);
-          const float* src = p.part_o + ((int64_t)(sb + sp) * kLargeRows + row) * D + d0;
-          const f32x4c a = *reinterpret_cast<const f32x4c*>(src);
-          const f32x4c b = *reinterpret_cast<const f32x4c*>(src + 4);
+      MergeState st;
+      st.m = ninf;
+      st.z = 0.f;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            o[k] += w * a[k];
-            o[4 + k] += w * b[k];
-          }
+      for (int k = 0; k < 8; ++k) st.o[k] = 0.f;
+      if (live) {
+        for (int sp = grp; sp < ns; sp += groups) {
+          const float ls = p.part_lse[(sb + sp) * kLargeRows + row];
+          merge_part(st, ls, p.part_o + ((int64_t)(sb + sp) * kLargeRows + row) * D + d0);
         }
       }
-      const int tok = x.q0 + x.t0 + row / p.G, head = x.g * p.G + row % p.G;
-      if constexpr (OUT_F32) {
-        float* dst = reinterpret_cast<float*>(p.out) + tok * p.o_st + head * p.o_sh + d0;
-        *reinterpret_cast<f32x4c*>(dst) = f32x4c{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4c*>(dst + 4) = f32x4c{o[4], o[5], o[6], o[7]};
-      } else {
-        char* dst = reinterpret_cast<char*>(p.out) + (tok * p.o_st + head * p.o_sh + d0) * 2;
-        *reinterpret_cast<u32x4c*>(dst) = u32x4c{pack_bf16x2_c(o[0], o[1]), pack_bf16x2_c(o[2], o[3]),
-                                                 pack_bf16x2_c(o[4], o[5]), pack_bf16x2_c(o[6], o[7])};
+      if (groups > 1) {
+        red[t] = st;
+        __syncthreads();
+        if (live && grp == 0)
+          for (int gq = 1; gq < groups; ++gq) merge_state(st, red[gq * per + idx]);
+        __syncthreads();
       }
-      if (d0 == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
+      if (live && grp == 0) {
+        const bool empty = !(st.z > 0.f);
+        const float inv = empty ? 0.f : 1.f / st.z;
+        const float lse = empty ? ninf : st.m + logf(st.z);
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = st.o[k] * inv;
+        const int tok = x.q0 + x.t0 + row / p.G, head = x.g * p.G + row % p.G;
+        if constexpr (OUT_F32) {
+          float* dst = reinterpret_cast<float*>(p.out) + tok * p.o_st + head * p.o_sh + d0;
+          *reinterpret_cast<f32x4c*>(dst) = f32x4c{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4c*>(dst + 4) = f32x4c{o[4], o[5], o[6], o[7]};
+        } else {
+          char* dst = reinterpret_cast<char*>(p.out) + (tok * p.o_st + head * p.o_sh + d0) * 2;
+          *reinterpret_cast<u32x4c*>(dst) = u32x4c{pack_bf16x2_c(o[0], o[1]), pack_bf16x2_c(o[2], o[3]),
+                                                   pack_bf16x2_c(o[4], o[5]), pack_bf16x2_c(o[6], o[7])};
+        }
+        if (d0 == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
+      }
     }
   }
 }

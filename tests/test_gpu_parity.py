@@ -142,6 +142,30 @@ def test_taskmap_bit_exact(make, workers, force):
     compare(b, out, lse)
 
 
+def test_block_mask_per_head_large():
+    """A per-query-head block mask, padded with unused key-tile columns past
+    64 KiB: Assign counts units from global memory (no LDS copy) and every
+    Q-block unions the masks of its G heads."""
+    import dataclasses
+    b = W.sparse_prefill(kind="bf16", seq_len=1024)
+    rng = np.random.default_rng(41)
+    B_, nq = b.num_seqs, b.block_mask.shape[2]
+    nk = 600                                   # 2 x 32 x 8 x 600 bytes > 64 KiB
+    m = (rng.random((B_, b.num_q_heads, nq, nk)) < 0.35).astype(np.uint8)
+    for t in range(nq):
+        m[:, :, t, t] = 1                      # keep the diagonal
+    b = dataclasses.replace(b, block_mask=torch.from_numpy(m))
+    assert m.nbytes > 64 * 1024
+    P = B.paged_attn_device_info(0)["default_workers"]
+    ref = oracle_taskmap(b, P)
+    g, out, lse, ws = gpu_run(b)
+    h, lay = header(ws, params_of(g))
+    assert h[7] == 0 and h[0] == ref["U"]
+    up = ws.cpu()[lay.unit_prefix:lay.unit_prefix + 4 * (ref["n_qb"] + 1)].view(torch.int32).numpy()
+    assert np.array_equal(up, ref["unit_prefix"])
+    compare(b, out, lse)
+
+
 def test_tiny_hybrid_f32():
     b = W.tiny_hybrid()
     P = B.paged_attn_device_info(0)["default_workers"]
