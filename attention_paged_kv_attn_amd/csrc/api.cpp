@@ -94,7 +94,7 @@ pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   size_t off = 0;
   L->header = off;        off = align256(off + pa::kHeaderInts * 4);
   L->seq_qb_base = off;   off = align256(off + size_t(p->num_seqs + 1) * 4);
-  L->qb_desc = off;       off = align256(off + size_t(n_qb_max) * 16);
+  L->qb_desc = off;       off = align256(off + size_t(n_qb_max) * 32);
   L->unit_prefix = off;   off = align256(off + size_t(n_qb_max + 1) * 4);
   L->n_splits = off;      off = align256(off + size_t(n_qb_max) * 4);
   L->slot_base = off;     off = align256(off + size_t(n_qb_max) * 4);

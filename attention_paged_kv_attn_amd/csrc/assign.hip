@@ -124,7 +124,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
     const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
     const int t0 = t * ntl;
     const int nt = min(ntl, ql - t0);
-    reinterpret_cast<int4*>(p.qb_desc)[q] = make_int4(b, g, t0, nt);
+    reinterpret_cast<int4*>(p.qb_desc)[2 * q] = make_int4(b, g, t0, nt);
+    reinterpret_cast<int4*>(p.qb_desc)[2 * q + 1] = make_int4(q0, ql, ctx, 0);   // saves the kernel two dependent loads
     const int pos_lo = ctx - ql + t0, pos_hi = pos_lo + nt - 1;
     int t_lo, t_hi, n = 0;
     if (qblock_tiles(p, ctx, pos_lo, pos_hi, t_lo, t_hi)) {

@@ -1316,12 +1316,19 @@ struct DirectStage {
   uint64_t ksp, vsp;          // bytes between pages
   uint32_t kss, vss;          // bytes between slots
   const int32_t* bt_row;
-  int pbase, vpage;
+  int pbase, vpage0, vpage1;  // page-table entries pbase + lane and pbase + 64 + lane
+  int cur_b, cur_g;
   // per lane: constant parts of the load offsets
   uint32_t k_col, v_col;      // byte column within a row
   int k_row0, v_row0;         // row of load i = 0 (K: + 16 i, V: + 16 i)
 
+  // (re)point at sequence s.b, kv head s.g; the page window survives while the
+  // sequence stays the same
   __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s) {
+    if (s.b == cur_b && s.g == cur_g) return;
+    if (s.b != cur_b) pbase = -(1 << 30);
+    cur_b = s.b;
+    cur_g = s.g;
     kbase = wave_uniform(reinterpret_cast<const char*>(p.k) + (int64_t)s.g * p.k_sh * 2);
     vbase = wave_uniform(reinterpret_cast<const char*>(p.v) + (int64_t)s.g * p.v_sh * 2);
     ksp = (uint64_t)p.k_sp * 2;
@@ -1329,8 +1336,6 @@ struct DirectStage {
     kss = (uint32_t)(p.k_ss * 2);
     vss = (uint32_t)(p.v_ss * 2);
     bt_row = s.bt_row;
-    pbase = -(1 << 30);
-    vpage = 0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, hh = lane >> 4;
     k_row0 = m;
@@ -1342,13 +1347,18 @@ struct DirectStage {
 
   __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
     const int idx = J0 >> p.page_shift;
-    if ((unsigned)(idx - pbase) >= 64u) {                // refill the window (rare)
+    if ((unsigned)(idx - pbase) >= 128u) {               // refill the window (rare)
       pbase = idx;
-      int v = bt_row[min(idx + (int)(threadIdx.x & 63), p.max_pages - 1)];
-      asm volatile("" : "+v"(v));                       // complete the load here
-      vpage = v;
+      const int l = (int)(threadIdx.x & 63);
+      int v0 = bt_row[min(idx + l, p.max_pages - 1)];
+      int v1 = bt_row[min(idx + 64 + l, p.max_pages - 1)];
+      asm volatile("" : "+v"(v0), "+v"(v1));           // complete the loads here
+      vpage0 = v0;
+      vpage1 = v1;
     }
-    int page = idx < p.max_pages ? __builtin_amdgcn_readlane(vpage, idx - pbase) : -1;
+    const int i = idx - pbase;
+    const int w0 = __builtin_amdgcn_readlane(vpage0, i & 63), w1 = __builtin_amdgcn_readlane(vpage1, i & 63);
+    int page = idx < p.max_pages ? (i < 64 ? w0 : w1) : -1;
     if ((unsigned)page >= (unsigned)p.num_pages) {
       p.hdr[H_ERROR] = E_PAGE;
       page = 0;
@@ -1396,7 +1406,7 @@ __device__ __forceinline__ bf16x8 v_operand_tr(const char* smem, uint32_t trx, u
 
 template <int KIND, int D, bool FAST>
 __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_lo, int t_hi, int u0,
-                                                       int u1, bool final_out, int slot) {
+                                                       int u1, bool final_out, int slot, DirectStage& ds) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const KParams& p = kparams_at(pk);
   using C = Cfg<KIND, D>;
@@ -1450,8 +1460,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   WaveState<KIND, D, NB> st;
   st.init();
   Stage<KIND, D, FAST> stg;
-  DirectStage ds;
-  if constexpr (DIRECT) ds.init(p, s);
+  if constexpr (DIRECT) ds.init(p, s);             // keeps its page window while the sequence stays
 
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
     const int cn = min(kMaskListCap, u1 - c0);
@@ -1639,6 +1648,10 @@ __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kerne
   const int G8 = gridDim.x / 8;
   const int rank = (gridDim.x % 8 == 0) ? (blockIdx.x % 8) * G8 + blockIdx.x / 8 : blockIdx.x;
   const int n_qb = p.hdr[H_NQB];
+  DirectStage ds;                                  // large segments' K/V addressing, kept across segments
+  ds.cur_b = -1;
+  ds.cur_g = -1;
+  ds.pbase = -(1 << 30);
   for (int vw = rank; vw < n_workers; vw += gridDim.x) {
     int a = vw * L;
     const int b_end = min(a + L, U);
@@ -1658,7 +1671,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kerne
         // the maximal run of small Q-blocks from here, inside this worker's range
         int run_end = S + u1, qq = q + 1;
         while (run_end < b_end && qq < n_qb) {
-          const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[qq];
+          const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[2 * qq];
           if (wave_uniform(d.w) * p.G > kSmallMaxRows) break;
           run_end = min(b_end, p.unit_prefix[qq + 1]);
           ++qq;
@@ -1674,7 +1687,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kerne
       const bool final_out = p.n_splits[q] == 1;
       const int slot = final_out ? 0 : p.slot_base[q] + (vw - S / L);
       if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
-      else large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
+      else large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot, ds);
       a = S + u1;
       ++q;
     }

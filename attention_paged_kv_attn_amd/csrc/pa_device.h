@@ -102,18 +102,21 @@ struct QBlock {
   int b, g, t0, nt, rows, ql, ctx, q0, pos_lo, pos_hi;
 };
 
+// The descriptor is 8 ints: b, g, t0, nt, then the sequence's q0, q_len and
+// seq_len (copied by Assign so one scalar load brings everything).
 __device__ __forceinline__ QBlock load_qblock(const KParams& p, int q) {
   QBlock x;
-  const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[q];
+  const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[2 * q];
+  const int4 e = reinterpret_cast<const int4*>(p.qb_desc)[2 * q + 1];
   // every lane of the wave reads the same descriptor: keep it in scalar registers
   x.b = __builtin_amdgcn_readfirstlane(d.x);
   x.g = __builtin_amdgcn_readfirstlane(d.y);
   x.t0 = __builtin_amdgcn_readfirstlane(d.z);
   x.nt = __builtin_amdgcn_readfirstlane(d.w);
   x.rows = x.nt * p.G;
-  x.q0 = __builtin_amdgcn_readfirstlane(p.qsl[x.b]);
-  x.ql = __builtin_amdgcn_readfirstlane(p.qsl[x.b + 1]) - x.q0;
-  x.ctx = __builtin_amdgcn_readfirstlane(p.seq_lens[x.b]);
+  x.q0 = __builtin_amdgcn_readfirstlane(e.x);
+  x.ql = __builtin_amdgcn_readfirstlane(e.y);
+  x.ctx = __builtin_amdgcn_readfirstlane(e.z);
   x.pos_lo = x.ctx - x.ql + x.t0;
   x.pos_hi = x.pos_lo + x.nt - 1;
   return x;

@@ -122,7 +122,7 @@ typedef struct pa_params {
 typedef struct pa_workspace_layout {
   size_t header;          /* int32[16]: U, P, L, n_qb, n_slots, n_combine, n_workers, error, max_slots */
   size_t seq_qb_base;     /* int32[B + 1]: first Q-block of each sequence */
-  size_t qb_desc;         /* int32[n_qb_max][4]: b, g, t0, nt */
+  size_t qb_desc;         /* int32[n_qb_max][8]: b, g, t0, nt, q0, q_len, seq_len, 0 */
   size_t unit_prefix;     /* int32[n_qb_max + 1] */
   size_t n_splits;        /* int32[n_qb_max] */
   size_t slot_base;       /* int32[n_qb_max], -1 when not split */

@@ -133,7 +133,12 @@ def test_taskmap_bit_exact(make, workers, force):
     assert h[7] == 0
     assert (h[0], h[1], h[2], h[3], h[4], h[5], h[6]) == (
         ref["U"], P, ref["L"], n, ref["n_slots"], len(ref["combine_list"]), ref["n_workers"])
-    assert np.array_equal(arr(lay.qb_desc, n, 4), ref["desc"])
+    desc = arr(lay.qb_desc, n, 8)
+    assert np.array_equal(desc[:, :4], ref["desc"])
+    qsl, ctx = b.query_start_loc.numpy(), b.seq_lens.numpy()
+    bb = ref["desc"][:, 0]
+    assert np.array_equal(desc[:, 4], qsl[bb]) and np.array_equal(desc[:, 5], qsl[bb + 1] - qsl[bb])
+    assert np.array_equal(desc[:, 6], ctx[bb]) and not desc[:, 7].any()
     assert np.array_equal(arr(lay.unit_prefix, n + 1), ref["unit_prefix"])
     assert np.array_equal(arr(lay.n_splits, n), ref["n_splits"])
     assert np.array_equal(arr(lay.slot_base, n), ref["slot_base"])
