@@ -1528,18 +1528,31 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
                 for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka[i], qB[nb][4 * cc + i], sc[nb][mb]);
             }
         } else {
+          // K operands stream from LDS KDEP reads ahead of the MFMAs that use
+          // them (the schedule groups below keep that order), so the reads'
+          // latency hides behind the matrix work instead of stalling each MFMA
+          constexpr int NK = 4 * C::KSQ, KDEP = 4;
+          using KT = typename QKOpT<KIND>::T;
+          auto kread = [&](int i) -> KT {
+            if constexpr (KIND == KIND_BF16)
+              return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + (i * 64 + lane) * 16));
+            else
+              return *reinterpret_cast<const long*>(kbuf + (i * 64 + lane) * 8);
+          };
+          KT kr[KDEP];
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int i = 0; i < KDEP; ++i) kr[i] = kread(i);
+          __builtin_amdgcn_sched_group_barrier(0x100, KDEP, 0);
 #pragma unroll
-            for (int ks = 0; ks < C::KSQ; ++ks) {
-              typename QKOpT<KIND>::T ka;
-              if constexpr (KIND == KIND_BF16)
-                ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + ((mb * C::KSQ + ks) * 64 + lane) * 16));
-              else
-                ka = *reinterpret_cast<const long*>(kbuf + ((mb * C::KSQ + ks) * 64 + lane) * 8);
+          for (int i = 0; i < NK; ++i) {
+            const KT ka = kr[i % KDEP];
+            if (i + KDEP < NK) kr[i % KDEP] = kread(i + KDEP);
+            const int mb = i / C::KSQ, ks = i % C::KSQ;
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
-            }
+            for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+            if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -1568,21 +1581,28 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
                     st.acc[nb][4 * gd + i] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], sc[nb][mb][j], st.acc[nb][4 * gd + i], 0, 0, 0);
               }
         } else if constexpr (DIRECT) {
+          // V^T operands by transpose reads, VDEP operands ahead of their MFMAs
+          constexpr int NV = 2 * MD, VDEP = 2;
+          auto vread = [&](int i) -> bf16x8 {
+            return v_operand_tr(smem, trx[i % MD], (uint32_t)(buf * C::STAGE + C::K_TILE + (i / MD) * 8192));
+          };
+          bf16x8 pb[2][NB];
 #pragma unroll
-          for (int ks2 = 0; ks2 < 2; ++ks2) {
-            bf16x8 pb[NB];
+          for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) pb[nb] = p_operand(sc[nb], ks2, vsc);
-            if constexpr (MSUM) {
+            for (int nb = 0; nb < NB; ++nb) pb[ks2][nb] = p_operand(sc[nb], ks2, vsc);
+          bf16x8 vr[VDEP];
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) st.lacc[nb] = mfma_pv(ones_bf16x8(), pb[nb], st.lacc[nb]);
-            }
+          for (int i = 0; i < VDEP; ++i) vr[i] = vread(i);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * VDEP, 0);
 #pragma unroll
-            for (int md = 0; md < MD; ++md) {
-              const bf16x8 va = v_operand_tr(smem, trx[md], (uint32_t)(buf * C::STAGE + C::K_TILE + ks2 * 8192));
+          for (int i = 0; i < NV; ++i) {
+            const bf16x8 va = vr[i % VDEP];
+            if (i + VDEP < NV) vr[i % VDEP] = vread(i + VDEP);
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) st.acc[nb][md] = mfma_pv(va, pb[nb], st.acc[nb][md]);
-            }
+            for (int nb = 0; nb < NB; ++nb) st.acc[nb][i % MD] = mfma_pv(va, pb[i / MD][nb], st.acc[nb][i % MD]);
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+            if (i + VDEP < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
         } else {
 #pragma unroll
