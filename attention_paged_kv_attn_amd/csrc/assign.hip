@@ -5,7 +5,8 @@
 // for the persistent split-K workgroups; §3.3: the chunk length is chosen from
 // the total load first, then each request is cut by its own KV length.  The
 // map is integer-only and must equal the CPU specification bit for bit:
-//   Q-blocks in (b, g, t0) order; n_units = active 64-key tiles; prefix S;
+//   Q-blocks in (b, g) order, a large Q-block's token blocks zig-zag
+//   (0, n-1, 1, n-2, ...); n_units = active 64-key tiles; prefix S;
 //   L = force ? force : max(L_min, ceil(U / P)); worker w owns [wL, (w+1)L);
 //   n_splits(q) = 0 | floor((S+n-1)/L) - floor(S/L) + 1; combine list = the
 //   Q-blocks with n_splits != 1; slot_base = running sum over split Q-blocks.
@@ -122,7 +123,9 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
     const int g = rem / per_g, t = rem % per_g;
     const int q0 = p.qsl[b], ql = p.qsl[b + 1] - q0, ctx = p.seq_lens[b];
     const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
-    const int t0 = t * ntl;
+    // zig-zag over the token blocks (spreads short and long Q-blocks evenly)
+    const int zi = (t & 1) ? per_g - 1 - (t >> 1) : (t >> 1);
+    const int t0 = zi * ntl;
     const int nt = min(ntl, ql - t0);
     reinterpret_cast<int4*>(p.qb_desc)[2 * q] = make_int4(b, g, t0, nt);
     reinterpret_cast<int4*>(p.qb_desc)[2 * q + 1] = make_int4(q0, ql, ctx, 0);   // saves the kernel two dependent loads

@@ -1531,7 +1531,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           // K operands stream from LDS KDEP reads ahead of the MFMAs that use
           // them (the schedule groups below keep that order), so the reads'
           // latency hides behind the matrix work instead of stalling each MFMA
-          constexpr int NK = 4 * C::KSQ, KDEP = 4;
+          constexpr int NK = 4 * C::KSQ, KDEP = 6;
           using KT = typename QKOpT<KIND>::T;
           auto kread = [&](int i) -> KT {
             if constexpr (KIND == KIND_BF16)
@@ -1582,7 +1582,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
               }
         } else if constexpr (DIRECT) {
           // V^T operands by transpose reads, VDEP operands ahead of their MFMAs
-          constexpr int NV = 2 * MD, VDEP = 2;
+          constexpr int NV = 2 * MD, VDEP = 3;
           auto vread = [&](int i) -> bf16x8 {
             return v_operand_tr(smem, trx[i % MD], (uint32_t)(buf * C::STAGE + C::K_TILE + (i / MD) * 8192));
           };

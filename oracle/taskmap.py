@@ -20,11 +20,15 @@ Pages followed:
 
 Specification
 -------------
-* Q-blocks, in (sequence b, kv head g, first token t0) order.  With
-  G = Hq / Hkv and q_len = query tokens of b: if q_len * G <= 16 the single
-  Q-block (b, g, 0, q_len) holds every query token of (b, g) ("small",
-  decode-like); otherwise Q-blocks hold nt = 128 / G tokens:
-  (b, g, t0, min(nt, q_len - t0)) for t0 = 0, nt, 2 nt, ... ("large").
+* Q-blocks, in (sequence b, kv head g) order.  With G = Hq / Hkv and
+  q_len = query tokens of b: if q_len * G <= 16 the single Q-block
+  (b, g, 0, q_len) holds every query token of (b, g) ("small",
+  decode-like); otherwise Q-blocks hold nt = 128 / G tokens,
+  (b, g, t0, min(nt, q_len - t0)), and the n = ceil(q_len / nt) token blocks
+  i = t0 / nt of one (b, g) are listed zig-zag: i = 0, n - 1, 1, n - 2, ...
+  ("large").  Under causal masking a token block's unit count grows with i,
+  so the zig-zag spreads short and long Q-blocks (and with them the fixed
+  cost each Q-block adds) evenly over the contiguous worker ranges below.
   Row r of a Q-block is token t0 + r // G, query head g * G + r % G.
 * A unit is one 64-key tile of one Q-block that holds at least one key some
   row of the Q-block may see (in the coarse sense below).  With
@@ -70,8 +74,11 @@ def q_blocks(seq_lens, query_start_loc, Hq, Hkv):
                 out.append((b, g, 0, ql))
         else:
             nt = LARGE_ROWS // G
+            n = -(-ql // nt)
             for g in range(Hkv):
-                for t0 in range(0, ql, nt):
+                for k in range(n):
+                    i = k // 2 if k % 2 == 0 else n - 1 - k // 2      # zig-zag over the token blocks
+                    t0 = i * nt
                     out.append((b, g, t0, min(nt, ql - t0)))
     return out
 

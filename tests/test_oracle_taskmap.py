@@ -112,3 +112,16 @@ def test_block_mask_unit_counts():
         # count is exact: tiles with a visible key under causal + mask
         want = _brute_units(tuple(desc), L_, L_, causal=True, mask=mask[b, 0].tolist())
         assert n == want
+
+
+def test_large_q_blocks_zigzag_and_cover_every_token_once():
+    # 300 query tokens at G = 4 -> token blocks of 32: n = 10 blocks per kv head
+    ctx = np.array([300, 1], dtype=np.int64)
+    qsl = np.array([0, 300, 301], dtype=np.int64)
+    qb = taskmap.q_blocks(ctx, qsl, Hq=8, Hkv=2)
+    seq0 = [d for d in qb if d[0] == 0 and d[1] == 1]
+    assert [d[2] // 32 for d in seq0] == [0, 9, 1, 8, 2, 7, 3, 6, 4, 5]
+    tokens = sorted(t for d in seq0 for t in range(d[2], d[2] + d[3]))
+    assert tokens == list(range(300)) and seq0[1][3] == 300 - 9 * 32
+    # decode sequence: one small Q-block per kv head
+    assert [d for d in qb if d[0] == 1] == [(1, 0, 0, 1), (1, 1, 0, 1)]
