@@ -188,6 +188,18 @@ __device__ __forceinline__ const char* wave_uniform(const char* ptr) {
   return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
+// A parameter held in a scalar register from here on.  Parameters are
+// invariant loads, so under register pressure the compiler would rather
+// re-load one inside a loop than keep it; each such load is followed by a
+// wait that also drains the loop's in-flight LDS reads.  The value an empty
+// asm hands back cannot be re-loaded, only kept (or spilled to a lane).
+__device__ __forceinline__ int held(int v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ float held(float v) { return __int_as_float(held(__float_as_int(v))); }
+
 // Loads at base + soff + voff: `base + soff` is wave-uniform (scalar), voff a
 // 32-bit per-lane offset, so the address is a scalar base plus a VGPR offset
 // when the compiler keeps the base in scalar registers.
@@ -344,12 +356,25 @@ struct RowMask {
   bool bit;         // block-mask bit of (row's query tile, the unit's key tile)
 };
 
+// The mask and scale parameters a tile loop tests on every tile.
+struct TileParams {
+  int causal, window, landmark, has_bm;
+  float sm_log2;
+  __device__ __forceinline__ static TileParams of(const KParams& p) {
+    return {p.causal, p.window, p.landmark, p.bm != nullptr, p.sm_log2};
+  }
+  // kept in registers for a whole segment (see held())
+  __device__ __forceinline__ static TileParams held_of(const KParams& p) {
+    return {held(p.causal), held(p.window), held(p.landmark), held((int)(p.bm != nullptr)), held(p.sm_log2)};
+  }
+};
+
 // Landmark keys (j + 1) % C == 0 inside the tile [J0, J0 + 64) as a bitmap over
 // key offsets; uniform across the workgroup.
-__device__ __forceinline__ uint64_t landmark_bits(const KParams& p, int J0) {
+__device__ __forceinline__ uint64_t landmark_bits(const TileParams& tp, int J0) {
   uint64_t m = 0;
-  if (p.landmark > 0) {
-    for (int o = p.landmark - 1 - (J0 % p.landmark); o < kUnitKeys; o += p.landmark) m |= 1ull << o;
+  if (tp.landmark > 0) {
+    for (int o = tp.landmark - 1 - (J0 % tp.landmark); o < kUnitKeys; o += tp.landmark) m |= 1ull << o;
   }
   return m;
 }
@@ -368,10 +393,10 @@ struct ElemMask {
   int lo;
   unsigned span;
   uint32_t l16;
-  __device__ __forceinline__ void init(const KParams& p, const RowMask& r, int J0, int nvalid, uint64_t lmk, int h) {
+  __device__ __forceinline__ void init(const TileParams& tp, const RowMask& r, int J0, int nvalid, uint64_t lmk, int h) {
     int hi = nvalid;
-    if (p.causal) hi = min(hi, r.pos - J0 + 1);
-    lo = p.window > 0 ? max(0, r.left - J0) : 0;
+    if (tp.causal) hi = min(hi, r.pos - J0 + 1);
+    lo = tp.window > 0 ? max(0, r.left - J0) : 0;
     span = (r.bit && hi > lo) ? (unsigned)(hi - lo) : 0u;
     l16 = lmk ? lane_bits16(lmk, h) : 0u;
   }
@@ -379,11 +404,11 @@ struct ElemMask {
 
 // The tile needs no causal, window, length or block-mask test for any row with
 // positions in [pos_min, ...] and window starts <= left_max (landmarks aside).
-__device__ __forceinline__ bool unit_is_full(const KParams& p, int J0, int nvalid, int pos_min, int left_max) {
+__device__ __forceinline__ bool unit_is_full(const TileParams& tp, int J0, int nvalid, int pos_min, int left_max) {
   if (nvalid < kUnitKeys) return false;
-  if (p.causal && J0 + kUnitKeys - 1 > pos_min) return false;
-  if (p.window > 0 && J0 < left_max) return false;
-  if (p.bm) return false;
+  if (tp.causal && J0 + kUnitKeys - 1 > pos_min) return false;
+  if (tp.window > 0 && J0 < left_max) return false;
+  if (tp.has_bm) return false;
   return true;
 }
 
@@ -796,13 +821,14 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) sc[mb] = mfma_qk(r.kA[mb][ks], qb, sc[mb]);
   }
-  const uint64_t lmk = landmark_bits(p, J0);
-  const bool full = unit_is_full(p, J0, tc.nvalid, pos_min, left_max);
-  float cs = p.sm_log2;
+  const TileParams tp = TileParams::of(p);
+  const uint64_t lmk = landmark_bits(tp, J0);
+  const bool full = unit_is_full(tp, J0, tc.nvalid, pos_min, left_max);
+  float cs = tp.sm_log2;
   if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
   if (!full) {
     ElemMask em;
-    em.init(p, rm, J0, tc.nvalid, lmk, h);
+    em.init(tp, rm, J0, tc.nvalid, lmk, h);
     mask_scores(sc, em, h);
   } else if (lmk) {
     mask_landmarks(sc, lmk, h);
@@ -1318,6 +1344,7 @@ struct DirectStage {
   const int32_t* bt_row;
   int pbase, vpage0, vpage1;  // page-table entries pbase + lane and pbase + 64 + lane
   int cur_b, cur_g;
+  int page_shift, max_pages, num_pages, page_mask;   // held (see held())
   // per lane: constant parts of the load offsets
   uint32_t k_col, v_col;      // byte column within a row
   int k_row0, v_row0;         // row of load i = 0 (K: + 16 i, V: + 16 i)
@@ -1329,6 +1356,10 @@ struct DirectStage {
     if (s.b != cur_b) pbase = -(1 << 30);
     cur_b = s.b;
     cur_g = s.g;
+    page_shift = held(p.page_shift);
+    max_pages = held(p.max_pages);
+    num_pages = held(p.num_pages);
+    page_mask = held(p.page_size - 1);
     kbase = wave_uniform(reinterpret_cast<const char*>(p.k) + (int64_t)s.g * p.k_sh * 2);
     vbase = wave_uniform(reinterpret_cast<const char*>(p.v) + (int64_t)s.g * p.v_sh * 2);
     ksp = (uint64_t)p.k_sp * 2;
@@ -1346,20 +1377,20 @@ struct DirectStage {
   }
 
   __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
-    const int idx = J0 >> p.page_shift;
+    const int idx = J0 >> page_shift;
     if ((unsigned)(idx - pbase) >= 128u) {               // refill the window (rare)
       pbase = idx;
       const int l = (int)(threadIdx.x & 63);
-      int v0 = bt_row[min(idx + l, p.max_pages - 1)];
-      int v1 = bt_row[min(idx + 64 + l, p.max_pages - 1)];
+      int v0 = bt_row[min(idx + l, max_pages - 1)];
+      int v1 = bt_row[min(idx + 64 + l, max_pages - 1)];
       asm volatile("" : "+v"(v0), "+v"(v1));           // complete the loads here
       vpage0 = v0;
       vpage1 = v1;
     }
     const int i = idx - pbase;
     const int w0 = __builtin_amdgcn_readlane(vpage0, i & 63), w1 = __builtin_amdgcn_readlane(vpage1, i & 63);
-    int page = idx < p.max_pages ? (i < 64 ? w0 : w1) : -1;
-    if ((unsigned)page >= (unsigned)p.num_pages) {
+    int page = idx < max_pages ? (i < 64 ? w0 : w1) : -1;
+    if ((unsigned)page >= (unsigned)num_pages) {
       p.hdr[H_ERROR] = E_PAGE;
       page = 0;
     }
@@ -1372,7 +1403,7 @@ struct DirectStage {
   __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
     const int J0 = tile * kUnitKeys;
     const int page = page_of_tile(p, J0);
-    const uint32_t slot = (uint32_t)(J0 & (p.page_size - 1));
+    const uint32_t slot = (uint32_t)(J0 & page_mask);
     const char* kb = wave_uniform(kbase + page * ksp + slot * kss);
     const char* vb = wave_uniform(vbase + page * vsp + slot * vss);
     const int lim = min(kUnitKeys, s.ctx - J0) - 1;
@@ -1417,7 +1448,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   // carries its rounding (up to 2^-9 on the largest term, which under the lazy
   // rescale is no longer exactly 1) straight into the LSE.
   constexpr bool MSUM = false;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is the same in every lane: scalar, so that per-wave bounds
+  // and the per-tile tests built on them are scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, h = lane >> 4;
   short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
   SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
@@ -1457,6 +1490,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     left_max = p.window > 0 ? window_left(p, pos_hi_w) : 0;
   }
 
+  const TileParams tp = TileParams::held_of(p);
   WaveState<KIND, D, NB> st;
   st.init();
   Stage<KIND, D, FAST> stg;
@@ -1464,10 +1498,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
 
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
     const int cn = min(kMaskListCap, u1 - c0);
-    if (p.bm) build_tile_list(p, x, t_lo, t_hi, c0, cn, list);
+    if (tp.has_bm) build_tile_list(p, x, t_lo, t_hi, c0, cn, list);
     auto tile_of = [&](int u) {   // wave-uniform: keeps tile addressing in scalar registers
-    return __builtin_amdgcn_readfirstlane(p.bm ? (int)list[u - c0] : t_lo + u);
-  };
+      return __builtin_amdgcn_readfirstlane(tp.has_bm ? (int)list[u - c0] : t_lo + u);
+    };
     if constexpr (DIRECT) {
       ds.load(p, s, tile_of(c0), smem, smem + C::K_TILE);
       wait_vmem();
@@ -1497,9 +1531,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       if (wave_live) {
         float vsc;
         const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
-        float cs = p.sm_log2;
+        float cs = tp.sm_log2;
         if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
-        if (p.bm) {
+        if (tp.has_bm) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const int kt = J0 / p.bm_tile, qt = rm[nb].pos / p.bm_tile;
@@ -1508,8 +1542,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           }
         }
         const int nvalid = min(kUnitKeys, x.ctx - J0);
-        const uint64_t lmk = landmark_bits(p, J0);
-        const bool full = unit_is_full(p, J0, nvalid, pos_min, left_max);
+        const uint64_t lmk = landmark_bits(tp, J0);
+        const bool full = unit_is_full(tp, J0, nvalid, pos_min, left_max);
         // S^T = K Q^T
         f32x4 sc[NB][4];
 #pragma unroll
@@ -1554,17 +1588,25 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
             if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
         }
+        if (!full || lmk != 0) {
+          // the lane bitmaps are built from an opaque copy of the landmark
+          // bits, so none of that work is hoisted onto the tiles that need
+          // no mask at all
+          uint64_t lm = lmk;
+          asm volatile("" : "+s"(lm));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if (!full) {
-            ElemMask em;
-            em.init(p, rm[nb], J0, nvalid, lmk, h);
-            mask_scores(sc[nb], em, h);
-          } else if (lmk) {
-            mask_landmarks(sc[nb], lmk, h);
+          for (int nb = 0; nb < NB; ++nb) {
+            if (!full) {
+              ElemMask em;
+              em.init(tp, rm[nb], J0, nvalid, lm, h);
+              mask_scores(sc[nb], em, h);
+            } else {
+              mask_landmarks(sc[nb], lm, h);
+            }
           }
-          softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], cs);
         }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], cs);
         // O^T += V^T P^T
         if constexpr (KIND == KIND_F32) {
 #pragma unroll
