@@ -69,6 +69,34 @@ struct Cfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+// bf16, d = 128, one page per tile (the direct path): the two V stages are LDS
+// arrays of their own (vstage), the rest stays in the dynamic block.  The
+// compiler then knows that a DMA into one V stage cannot touch the transpose
+// reads of the other and issues those reads without waiting for every DMA in
+// flight.  Small ranges keep four of their eight stash pieces in the V stages.
+constexpr int kVStageBytes = 16384;
+template <int KIND, int D, bool FAST>
+struct Lds {
+  using C = Cfg<KIND, D>;
+  static constexpr bool SPLIT_V = KIND == KIND_BF16 && D == 128 && FAST;
+  static constexpr int STASH_PIECES_DYN = SPLIT_V ? kWaves : 2 * kWaves;      // acc pieces in the dynamic block
+  static constexpr int STASH_DYN = (2 * 2 * kWaves * 16 + STASH_PIECES_DYN * 16 * D) * 4 + 2 * kWaves * 4;
+  static constexpr int BODY = SPLIT_V ? (2 * C::K_TILE > C::QOFF + C::QBYTES ? 2 * C::K_TILE : C::QOFF + C::QBYTES)
+                                      : C::BODY0;
+  static constexpr int DYN = (BODY > STASH_DYN ? BODY : STASH_DYN) + kMaskListCap * 2;
+  static constexpr int TOTAL = DYN + (SPLIT_V ? 2 * kVStageBytes : 0);
+  static constexpr int OCC = TOTAL <= 80 * 1024 ? 2 : 1;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(!SPLIT_V || 2 * 16 * D * 4 <= kVStageBytes, "two stash pieces per V stage");
+};
+
+template <bool ON>
+__device__ __forceinline__ char* vstage(int i) {
+  __shared__ __attribute__((aligned(16))) char v0[ON ? kVStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) char v1[ON ? kVStageBytes : 16];
+  return i ? v1 : v0;
+}
+
 template <int KIND> struct QKOpT;
 template <> struct QKOpT<KIND_F32> { using T = float; };
 template <> struct QKOpT<KIND_BF16> { using T = bf16x8; };
@@ -888,7 +916,7 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
   constexpr int MD = C::MD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, h = lane >> 4;
-  short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
+  short* list = reinterpret_cast<short*>(smem + Lds<KIND, D, FAST>::DYN - kMaskListCap * 2);
 
   SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
   // this lane's query row
@@ -1015,14 +1043,23 @@ struct StreamCursor {
   QBlock x;
   int pbase;     // page-table index held by lane 0 of vpage
   int vpage;
+  int nE;        // unit_prefix[q + 2], loaded ahead of the next Q-block change
 };
 
-template <int KIND, int D>
+template <int KIND, int D, bool FAST>
 struct StashLayout {   // 8 pieces (2 per wave): m[16], l[16], acc[16][D] (raw), tag
   static constexpr int PIECES = 2 * kWaves;
+  static constexpr bool SPLIT = Lds<KIND, D, FAST>::SPLIT_V;
   static constexpr int M = 0, Lf = PIECES * 16, ACC = 2 * PIECES * 16;
-  static constexpr int FLOATS = ACC + PIECES * 16 * D;
-  static constexpr int BYTES = FLOATS * 4 + PIECES * 4;
+  static constexpr int FLOATS = ACC + Lds<KIND, D, FAST>::STASH_PIECES_DYN * 16 * D;
+  // raw accumulator of piece k: in the dynamic block, or (split) pieces
+  // kWaves.. two to a V stage
+  __device__ __forceinline__ static float* acc(float* stash, int k) {
+    if constexpr (SPLIT) {
+      if (k >= kWaves) return reinterpret_cast<float*>(vstage<true>((k - kWaves) >> 1)) + ((k - kWaves) & 1) * 16 * D;
+    }
+    return stash + ACC + k * 16 * D;
+  }
 };
 
 template <int KIND, int D, bool FAST>
@@ -1030,15 +1067,36 @@ __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c
                                                int u, int n, int h, int lane) {
   using C = Cfg<KIND, D>;
   if (u >= c.E) {                                        // next Q-block (rare: scalar loads)
-    int q = c.q;
-    while (p.unit_prefix[q + 1] <= u) ++q;
+    const int b_prev = c.E < 0 ? -1 : c.x.b;
+    int q;
+    if (c.E < 0) {                                       // first unit of the range
+      q = c.q;
+      while (p.unit_prefix[q + 1] <= u) ++q;
+      q = wave_uniform(q);
+      c.x = load_qblock(p, q);
+      c.S = wave_uniform(p.unit_prefix[q]);
+      c.E = wave_uniform(p.unit_prefix[q + 1]);
+    } else {
+      // the end of q + 1 was loaded ahead; Q-blocks without units are skipped
+      q = c.q + 1;
+      int S = c.E, E = c.nE;
+      while (E <= u) {
+        ++q;
+        S = E;
+        E = p.unit_prefix[q + 1];
+      }
+      // small Q-blocks of one sequence are its kv heads in order: the next
+      // one differs only in g, otherwise its descriptor is loaded
+      if (q == c.q + 1 && c.x.g + 1 < p.Hkv) c.x.g += 1;
+      else c.x = load_qblock(p, wave_uniform(q));
+      c.S = wave_uniform(S);
+      c.E = wave_uniform(E);
+    }
     c.q = wave_uniform(q);
-    c.x = load_qblock(p, c.q);
-    c.S = wave_uniform(p.unit_prefix[c.q]);
-    c.E = wave_uniform(p.unit_prefix[c.q + 1]);
+    c.nE = c.q + 2 <= p.hdr[H_NQB] ? p.unit_prefix[c.q + 2] : 0x7fffffff;
     int t_hi;
     qblock_tiles(p, c.x.ctx, c.x.pos_lo, c.x.pos_hi, c.t_lo, t_hi);
-    c.pbase = -(1 << 30);
+    if (c.x.b != b_prev) c.pbase = -(1 << 30);           // the page window stays with its sequence
   }
   const QBlock& x = c.x;
   SeqCtx s{x.b, x.g, x.ctx, c.t_lo, p.bt + (int64_t)x.b * p.bt_stride};
@@ -1082,7 +1140,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const KParams& p = kparams_at(pk);
   using C = Cfg<KIND, D>;
-  using SL = StashLayout<KIND, D>;
+  using SL = StashLayout<KIND, D, FAST>;
   constexpr int MD = C::MD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, h = lane >> 4;
@@ -1120,7 +1178,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int md = 0; md < MD; ++md) stash[SL::ACC + (k * 16 + n) * D + out_dim<KIND, D>(h, j, md)] = st.acc[0][md][j];
+          for (int md = 0; md < MD; ++md) SL::acc(stash, k)[n * D + out_dim<KIND, D>(h, j, md)] = st.acc[0][md][j];
       }
     };
     auto consume = [&](const StreamRec<KIND, D, FAST>& rec) {
@@ -1184,7 +1242,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
           const float c = __builtin_amdgcn_exp2f(stash[SL::M + j * 16 + row] - M);
           Ls += stash[SL::Lf + j * 16 + row] * c;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] += stash[SL::ACC + (j * 16 + row) * D + d0 + i] * c;
+          for (int i = 0; i < 8; ++i) o[i] += SL::acc(stash, j)[row * D + d0 + i] * c;
         }
       }
       const bool empty = !(Ls > 0.f);
@@ -1400,19 +1458,29 @@ struct DirectStage {
   // K in MFMA-operand order at kbuf + 1024 (4 mb + ks); V row-major, 16-byte
   // columns swizzled by row, at vbuf.  Rows past the sequence end re-read its
   // last key (finite values; their scores are masked).
-  __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
+  const char* pk_b;
+  const char* pv_b;
+  int plim;
+  // The addresses of one tile's DMAs; issue(i) then starts DMA i of 8 (K rows
+  // for i < 4, V rows after).  A DMA holds its wave until the address unit
+  // takes it, so the tile loop spreads the eight over its QK MFMAs.
+  __device__ __forceinline__ void prep(const KParams& p, const SeqCtx& s, int tile) {
     const int J0 = tile * kUnitKeys;
     const int page = page_of_tile(p, J0);
     const uint32_t slot = (uint32_t)(J0 & page_mask);
-    const char* kb = wave_uniform(kbase + page * ksp + slot * kss);
-    const char* vb = wave_uniform(vbase + page * vsp + slot * vss);
-    const int lim = min(kUnitKeys, s.ctx - J0) - 1;
+    pk_b = wave_uniform(kbase + page * ksp + slot * kss);
+    pv_b = wave_uniform(vbase + page * vsp + slot * vss);
+    plim = min(kUnitKeys, s.ctx - J0) - 1;
+  }
+  __device__ __forceinline__ void issue(int i, char* kbuf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (i < 4) gload16_lds(pk_b, kbuf + 1024 * (4 * i + wave), (uint32_t)min(k_row0 + 16 * i, plim) * kss + k_col, 0u);
+    else gload16_lds(pv_b, vbuf + 1024 * (4 * (i - 4) + wave), (uint32_t)min(v_row0 + 16 * (i - 4), plim) * vss + v_col, 0u);
+  }
+  __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
+    prep(p, s, tile);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gload16_lds(kb, kbuf + 1024 * (4 * i + wave), (uint32_t)min(k_row0 + 16 * i, lim) * kss + k_col, 0u);
-      gload16_lds(vb, vbuf + 1024 * (4 * i + wave), (uint32_t)min(v_row0 + 16 * i, lim) * vss + v_col, 0u);
-    }
+    for (int i = 0; i < 8; ++i) issue(i, kbuf, vbuf);
   }
 };
 
@@ -1452,7 +1520,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   // and the per-tile tests built on them are scalar branches
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, h = lane >> 4;
-  short* list = reinterpret_cast<short*>(smem + C::LDS - kMaskListCap * 2);
+  short* list = reinterpret_cast<short*>(smem + Lds<KIND, D, FAST>::DYN - kMaskListCap * 2);
   SeqCtx s{x.b, x.g, x.ctx, t_lo, p.bt + (int64_t)x.b * p.bt_stride};
   // transpose-read lane offsets (see v_operand_tr), relative to a V buffer
   const int trk = n >> 2, trc = n & 3;
@@ -1503,7 +1571,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       return __builtin_amdgcn_readfirstlane(tp.has_bm ? (int)list[u - c0] : t_lo + u);
     };
     if constexpr (DIRECT) {
-      ds.load(p, s, tile_of(c0), smem, smem + C::K_TILE);
+      ds.load(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
     } else {
       stg.load(p, s, tile_of(c0));
@@ -1514,16 +1582,22 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     // LDS address is a lane register plus an immediate offset
     auto step = [&](int u, auto buf_c) {
       constexpr int buf = decltype(buf_c)::value;
-      char* kbuf = smem + buf * C::STAGE;
+      char* kbuf = DIRECT ? smem + buf * C::K_TILE : smem + buf * C::STAGE;
       char* vbuf = kbuf + C::K_TILE;
       const bool more = u + 1 < c0 + cn;
-      if (more) {
-        if constexpr (DIRECT) {
-          char* nk = smem + (buf ^ 1) * C::STAGE;
-          ds.load(p, s, tile_of(u + 1), nk, nk + C::K_TILE);
-        } else {
-          stg.load(p, s, tile_of(u + 1));
+      char* nkb = smem + (buf ^ 1) * C::K_TILE;
+      char* nvb = nullptr;
+      if constexpr (DIRECT) {
+        // the next tile's DMAs go out between the QK MFMAs below (the last
+        // step of a chunk re-loads its own tile into the idle stage)
+        nvb = vstage<true>(buf ^ 1);
+        ds.prep(p, s, tile_of(more ? u + 1 : u));
+        if (!wave_live) {                               // a wave with no rows still loads its share
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ds.issue(i, nkb, nvb);
         }
+      } else if (more) {
+        stg.load(p, s, tile_of(u + 1));
       }
       __builtin_amdgcn_sched_barrier(0);
       const int tile = tile_of(u);
@@ -1584,10 +1658,16 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
             const int mb = i / C::KSQ, ks = i % C::KSQ;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
+            if constexpr (DIRECT) { if (i % 2 == 1) ds.issue(i / 2, nkb, nvb); }
             __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
             if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if constexpr (DIRECT) { if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); }
           }
         }
+        // the softmax (VALU work) runs at raised wave priority, so on a SIMD
+        // shared with the other workgroup's wave it goes ahead of that wave's
+        // matrix work instead of queueing behind it (measured faster)
+        __builtin_amdgcn_s_setprio(1);
         if (!full || lmk != 0) {
           // the lane bitmaps are built from an opaque copy of the landmark
           // bits, so none of that work is hoisted onto the tiles that need
@@ -1607,6 +1687,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], cs);
+        __builtin_amdgcn_s_setprio(0);
         // O^T += V^T P^T
         if constexpr (KIND == KIND_F32) {
 #pragma unroll
@@ -1624,9 +1705,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
               }
         } else if constexpr (DIRECT) {
           // V^T operands by transpose reads, VDEP operands ahead of their MFMAs
-          constexpr int NV = 2 * MD, VDEP = 3;
+          constexpr int NV = 2 * MD, VDEP = 8;
           auto vread = [&](int i) -> bf16x8 {
-            return v_operand_tr(smem, trx[i % MD], (uint32_t)(buf * C::STAGE + C::K_TILE + (i / MD) * 8192));
+            return v_operand_tr(vstage<true>(buf), trx[i % MD], (uint32_t)((i / MD) * 8192));
           };
           bf16x8 pb[2][NB];
 #pragma unroll
@@ -1667,7 +1748,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (DIRECT) {
-        if (more) wait_vmem();
+        wait_vmem();
       } else if (more) {
         char* nk = smem + (buf ^ 1) * C::STAGE;
         stg.store(nk, nk + C::K_TILE);
@@ -1697,7 +1778,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
 // ---------------------------------------------------------------------------
 
 template <int KIND, int D, bool FAST>
-__global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kernel(KParams) {
+__global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention_kernel(KParams) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t pk = kparams_addr();
   const KParams& p = kparams_at(pk);
@@ -1758,7 +1839,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<KIND, D>::OCC)) void attention_kerne
 
 template <int KIND, int D, bool FAST>
 static hipError_t launch_attention_t(const KParams& p, int grid, hipStream_t stream) {
-  const int lds = Cfg<KIND, D>::LDS;
+  const int lds = Lds<KIND, D, FAST>::DYN;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST>),

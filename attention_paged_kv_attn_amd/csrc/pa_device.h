@@ -106,17 +106,18 @@ struct QBlock {
 // seq_len (copied by Assign so one scalar load brings everything).
 __device__ __forceinline__ QBlock load_qblock(const KParams& p, int q) {
   QBlock x;
-  const int4 d = reinterpret_cast<const int4*>(p.qb_desc)[2 * q];
-  const int4 e = reinterpret_cast<const int4*>(p.qb_desc)[2 * q + 1];
-  // every lane of the wave reads the same descriptor: keep it in scalar registers
-  x.b = __builtin_amdgcn_readfirstlane(d.x);
-  x.g = __builtin_amdgcn_readfirstlane(d.y);
-  x.t0 = __builtin_amdgcn_readfirstlane(d.z);
-  x.nt = __builtin_amdgcn_readfirstlane(d.w);
+  // scalar loads: the descriptor is the same for the whole wave, and a scalar
+  // load does not wait on the wave's vector loads in flight
+  typedef int cint __attribute__((address_space(4)));
+  const cint* dp = (const cint*)(p.qb_desc + 8 * (int64_t)q);
+  x.b = dp[0];
+  x.g = dp[1];
+  x.t0 = dp[2];
+  x.nt = dp[3];
   x.rows = x.nt * p.G;
-  x.q0 = __builtin_amdgcn_readfirstlane(e.x);
-  x.ql = __builtin_amdgcn_readfirstlane(e.y);
-  x.ctx = __builtin_amdgcn_readfirstlane(e.z);
+  x.q0 = dp[4];
+  x.ql = dp[5];
+  x.ctx = dp[6];
   x.pos_lo = x.ctx - x.ql + x.t0;
   x.pos_hi = x.pos_lo + x.nt - 1;
   return x;
