@@ -1,4 +1,5 @@
-// assign.hip — the Assign stage: one workgroup builds the task map.
+// assign.hip — the Assign stage: one workgroup builds the task map (with a
+// block mask, a grid counts the units between its two halves).
 //
 // "Triton-TLE rewrite of Tencent HPC-Ops Attention", §1.2: Assign cuts every
 // KV sequence into tiles and produces a load-balanced, GPU-resident task map
@@ -10,17 +11,13 @@
 //   L = force ? force : max(L_min, ceil(U / P)); worker w owns [wL, (w+1)L);
 //   n_splits(q) = 0 | floor((S+n-1)/L) - floor(S/L) + 1; combine list = the
 //   Q-blocks with n_splits != 1; slot_base = running sum over split Q-blocks.
+#include <algorithm>
+
 #include "pa_device.h"
 
 namespace pa {
 
 constexpr int kAssignThreads = 1024;
-constexpr int kAssignMaskLds = 64 * 1024;   // block masks up to this many bytes are staged in LDS
-
-// Bytes of the block mask as a dense [B, H_m, n_q_tiles, n_k_tiles] array.
-__host__ __device__ inline long long mask_elems(const KParams& p) {
-  return p.bm == nullptr ? 0 : (long long)p.B * p.bm_heads * p.bm_nq * p.bm_nk;
-}
 
 // Exclusive prefix sum over the workgroup; *total gets the sum.  `sh` holds
 // kAssignThreads / 64 + 1 ints of LDS.
@@ -51,46 +48,28 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh) 
   return base + x - v;
 }
 
-__global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
-  __shared__ int sh[kAssignThreads / 64 + 1];
-  __shared__ int err;
-  extern __shared__ uint8_t mask_lds[];
+// Steps 0 and 1 (one workgroup): metadata checks, then the first Q-block of
+// every sequence.  Returns n_qb, or -1 after writing an error header.
+__device__ int assign_sequences(const KParams& p, int* sh, int* err) {
   const int tid = threadIdx.x;
-  if (tid == 0) err = E_NONE;
-  // A small block mask is copied into LDS first (independent byte loads from
-  // every thread) so that the per-Q-block tile counts below read LDS instead of
-  // issuing one dependent global load per tile.
-  const long long melems = mask_elems(p);
-  const bool staged = melems > 0 && melems <= kAssignMaskLds;
-  if (staged) {
-    for (int i = tid; i < (int)melems; i += kAssignThreads) {
-      int r = i;
-      const int kt = r % p.bm_nk; r /= p.bm_nk;
-      const int qt = r % p.bm_nq; r /= p.bm_nq;
-      const int hm = r % p.bm_heads;
-      const int b = r / p.bm_heads;
-      mask_lds[i] = p.bm[b * p.bm_sb + hm * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
-    }
-  }
+  if (tid == 0) *err = E_NONE;
   __syncthreads();
-
   // 0. metadata checks: qsl is a non-decreasing prefix ending at total_q, q_len <= seq_len
   for (int b = tid; b < p.B; b += kAssignThreads) {
     const int a = p.qsl[b], c = p.qsl[b + 1];
-    if ((b == 0 && a != 0) || c < a || (b == p.B - 1 && c != p.total_q)) atomicMax(&err, (int)E_QSL);
-    else if (c - a > p.seq_lens[b]) atomicMax(&err, (int)E_QLEN);
+    if ((b == 0 && a != 0) || c < a || (b == p.B - 1 && c != p.total_q)) atomicMax(err, (int)E_QSL);
+    else if (c - a > p.seq_lens[b]) atomicMax(err, (int)E_QLEN);
   }
   __syncthreads();
-  if (err != E_NONE) {
+  if (*err != E_NONE) {
     if (tid == 0) {
       for (int i = 0; i < kHeaderInts; ++i) p.hdr[i] = 0;
       p.hdr[H_P] = p.P;
-      p.hdr[H_ERROR] = err;
+      p.hdr[H_ERROR] = *err;
       p.hdr[H_MAXSLOTS] = p.max_slots;
     }
-    return;
+    return -1;
   }
-
   // 1. Q-blocks per sequence -> first Q-block index of each sequence
   const int nt_large = kLargeRows / p.G;
   int carry = 0, tot;
@@ -107,56 +86,48 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
     carry += tot;
   }
   if (tid == 0) p.seq_qb_base[p.B] = carry;
-  const int n_qb = carry;
   __syncthreads();
+  return carry;
+}
 
-  // 2. descriptors and unit counts (counts parked in unit_prefix[q + 1])
-  for (int q = tid; q < n_qb; q += kAssignThreads) {
-    int lo = 0, hi = p.B - 1;                      // last b with base[b] <= q
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.seq_qb_base[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int per_g = (p.seq_qb_base[b + 1] - p.seq_qb_base[b]) / p.Hkv;
-    const int rem = q - p.seq_qb_base[b];
-    const int g = rem / per_g, t = rem % per_g;
-    const int q0 = p.qsl[b], ql = p.qsl[b + 1] - q0, ctx = p.seq_lens[b];
-    const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
-    // zig-zag over the token blocks (spreads short and long Q-blocks evenly)
-    const int zi = (t & 1) ? per_g - 1 - (t >> 1) : (t >> 1);
-    const int t0 = zi * ntl;
-    const int nt = min(ntl, ql - t0);
-    reinterpret_cast<int4*>(p.qb_desc)[2 * q] = make_int4(b, g, t0, nt);
-    reinterpret_cast<int4*>(p.qb_desc)[2 * q + 1] = make_int4(q0, ql, ctx, 0);   // saves the kernel two dependent loads
-    const int pos_lo = ctx - ql + t0, pos_hi = pos_lo + nt - 1;
-    int t_lo, t_hi, n = 0;
-    if (qblock_tiles(p, ctx, pos_lo, pos_hi, t_lo, t_hi)) {
-      if (p.bm == nullptr) {
-        n = t_hi - t_lo + 1;
-      } else {
-        // walk the mask columns kt (T = block_mask_tile keys = upt 64-key
-        // tiles): a set column adds its tiles that lie in [t_lo, t_hi]
-        const int upt = p.bm_tile / kUnitKeys;
-        const int kt_lo = t_lo / upt, kt_hi = min(t_hi / upt, p.bm_nk - 1);
-        const int qt0 = pos_lo / p.bm_tile, qt1 = min(pos_hi / p.bm_tile, p.bm_nq - 1);
-        const int h0 = p.bm_heads == 1 ? 0 : g * p.G, h1 = p.bm_heads == 1 ? 1 : (g + 1) * p.G;
-        for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-          bool on = false;
-          for (int hm = h0; hm < h1 && !on; ++hm)
-            for (int qt = qt0; qt <= qt1 && !on; ++qt)
-              on = staged ? mask_lds[(((long long)b * p.bm_heads + hm) * p.bm_nq + qt) * p.bm_nk + kt] != 0
-                          : p.bm[b * p.bm_sb + hm * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
-          if (on) n += min(t_hi, kt * upt + upt - 1) - max(t_lo, kt * upt) + 1;
-        }
-      }
-    }
-    p.unit_prefix[q + 1] = n;
+// Step 2 for one Q-block: its descriptor (written) and its tile range.
+struct QbTiles {
+  int b, g, pos_lo, pos_hi, t_lo, t_hi;
+  bool any;
+};
+__device__ __forceinline__ QbTiles assign_descriptor(const KParams& p, int q) {
+  int lo = 0, hi = p.B - 1;                        // last b with base[b] <= q
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.seq_qb_base[mid] <= q) lo = mid; else hi = mid - 1;
   }
-  __syncthreads();
+  const int b = lo;
+  const int nt_large = kLargeRows / p.G;
+  const int per_g = (p.seq_qb_base[b + 1] - p.seq_qb_base[b]) / p.Hkv;
+  const int rem = q - p.seq_qb_base[b];
+  const int g = rem / per_g, t = rem % per_g;
+  const int q0 = p.qsl[b], ql = p.qsl[b + 1] - q0, ctx = p.seq_lens[b];
+  const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
+  // zig-zag over the token blocks (spreads short and long Q-blocks evenly)
+  const int zi = (t & 1) ? per_g - 1 - (t >> 1) : (t >> 1);
+  const int t0 = zi * ntl;
+  const int nt = min(ntl, ql - t0);
+  reinterpret_cast<int4*>(p.qb_desc)[2 * q] = make_int4(b, g, t0, nt);
+  reinterpret_cast<int4*>(p.qb_desc)[2 * q + 1] = make_int4(q0, ql, ctx, 0);   // saves the kernel two dependent loads
+  QbTiles r;
+  r.b = b;
+  r.g = g;
+  r.pos_lo = ctx - ql + t0;
+  r.pos_hi = r.pos_lo + nt - 1;
+  r.any = qblock_tiles(p, ctx, r.pos_lo, r.pos_hi, r.t_lo, r.t_hi);
+  return r;
+}
 
+// Steps 3 and 4 (one workgroup): unit prefix, L, splits, combine list, slots, header.
+__device__ void assign_splits(const KParams& p, int n_qb, int* sh) {
+  const int tid = threadIdx.x;
   // 3. unit prefix
-  carry = 0;
+  int carry = 0, tot;
   for (int c0 = 0; c0 < n_qb; c0 += kAssignThreads) {
     const int q = c0 + tid;
     const int n = q < n_qb ? p.unit_prefix[q + 1] : 0;
@@ -205,17 +176,92 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
   }
 }
 
-hipError_t launch_assign(const KParams& p, hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&assign_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kAssignMaskLds);
-    if (e != hipSuccess) return e;
-    configured = true;
+// Without a block mask: one workgroup does every step (unit counts are closed forms).
+__global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
+  __shared__ int sh[kAssignThreads / 64 + 1];
+  __shared__ int err;
+  const int n_qb = assign_sequences(p, sh, &err);
+  if (n_qb < 0) return;
+  // 2. descriptors and unit counts (counts parked in unit_prefix[q + 1])
+  for (int q = threadIdx.x; q < n_qb; q += kAssignThreads) {
+    const QbTiles r = assign_descriptor(p, q);
+    p.unit_prefix[q + 1] = r.any ? r.t_hi - r.t_lo + 1 : 0;
   }
-  const long long me = mask_elems(p);
-  const int lds = (me > 0 && me <= kAssignMaskLds) ? (int)((me + 15) & ~15LL) : 0;
-  hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), lds, stream, p);
+  __syncthreads();
+  assign_splits(p, n_qb, sh);
+}
+
+// With a block mask the unit counts are the expensive part, so they get a
+// grid of their own between the two single-workgroup halves: one wave per
+// Q-block, its lanes over the mask columns (independent loads, summed by a
+// wave reduction).  The halves pass their state through the workspace: the
+// first leaves n_qb in seq_qb_base[B] and E_NONE in the error word.
+__global__ __launch_bounds__(kAssignThreads) void assign_begin_kernel(KParams p) {
+  __shared__ int sh[kAssignThreads / 64 + 1];
+  __shared__ int err;
+  const int n_qb = assign_sequences(p, sh, &err);
+  if (n_qb >= 0 && threadIdx.x == 0) p.hdr[H_ERROR] = E_NONE;
+}
+
+constexpr int kCountThreads = 256;
+
+__global__ __launch_bounds__(kCountThreads) void assign_count_kernel(KParams p) {
+  if (p.hdr[H_ERROR] != E_NONE) return;
+  const int n_qb = p.seq_qb_base[p.B];
+  const int lane = threadIdx.x & 63;
+  const int waves = kCountThreads / 64;
+  const int upt = p.bm_tile / kUnitKeys;
+  for (int q = blockIdx.x * waves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); q < n_qb; q += gridDim.x * waves) {
+    QbTiles r;
+    if (lane == 0) r = assign_descriptor(p, q);
+    r.b = __shfl(r.b, 0);
+    r.g = __shfl(r.g, 0);
+    r.pos_lo = __shfl(r.pos_lo, 0);
+    r.pos_hi = __shfl(r.pos_hi, 0);
+    r.t_lo = __shfl(r.t_lo, 0);
+    r.t_hi = __shfl(r.t_hi, 0);
+    r.any = __shfl((int)r.any, 0) != 0;
+    int cnt = 0;
+    if (r.any) {
+      // a mask column kt (block_mask_tile keys = upt 64-key tiles) that is set
+      // for some head and query tile of the Q-block adds its tiles in [t_lo, t_hi]
+      const int kt_lo = r.t_lo / upt, kt_hi = min(r.t_hi / upt, p.bm_nk - 1);
+      const int qt0 = r.pos_lo / p.bm_tile, qt1 = min(r.pos_hi / p.bm_tile, p.bm_nq - 1);
+      const int h0 = p.bm_heads == 1 ? 0 : r.g * p.G, h1 = p.bm_heads == 1 ? 1 : (r.g + 1) * p.G;
+      const uint8_t* base = p.bm + r.b * p.bm_sb;
+      for (int kt = kt_lo + lane; kt <= kt_hi; kt += 64) {
+        bool on = false;
+        for (int hm = h0; hm < h1; ++hm)
+          for (int qt = qt0; qt <= qt1; ++qt) on |= base[hm * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
+        if (on) cnt += min(r.t_hi, kt * upt + upt - 1) - max(r.t_lo, kt * upt) + 1;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d);
+    if (lane == 0) p.unit_prefix[q + 1] = cnt;
+  }
+}
+
+__global__ __launch_bounds__(kAssignThreads) void assign_end_kernel(KParams p) {
+  __shared__ int sh[kAssignThreads / 64 + 1];
+  if (p.hdr[H_ERROR] != E_NONE) return;
+  assign_splits(p, p.seq_qb_base[p.B], sh);
+}
+
+hipError_t launch_assign(const KParams& p, hipStream_t stream) {
+  if (p.bm == nullptr) {
+    hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(assign_begin_kernel, dim3(1), dim3(kAssignThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int waves = kCountThreads / 64;
+  const int grid = (int)std::min<long long>(4096, ((long long)p.n_qb_max + waves - 1) / waves);
+  hipLaunchKernelGGL(assign_count_kernel, dim3(grid > 0 ? grid : 1), dim3(kCountThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(assign_end_kernel, dim3(1), dim3(kAssignThreads), 0, stream, p);
   return hipGetLastError();
 }
 
