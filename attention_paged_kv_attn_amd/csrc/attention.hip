@@ -121,18 +121,13 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// Two E4M3FN bytes (bits 0-7 and 8-15 of w) -> two bf16 in one word, exactly.
-// The byte's low 7 bits placed at float bits 20..26 form the float
-// 2^(e-127) * 1.m (e >= 1) or the denormal m * 2^-129 (e == 0); scaling by
-// 2^120 gives 2^(e-7) * 1.m or m * 2^-9, the E4M3 value.  Four significant
-// bits fit bf16 exactly, so the top half of the float is the bf16.
-// (NaN codes map to 480; they only occur in slots that are never visible and
-// are zeroed before use.)
+// Two E4M3FN bytes of w (bits 0-15, or 16-31 with HI) -> two bf16 in one
+// word, exactly (every E4M3FN value is a bf16), by the hardware conversion
+// at scale 1.  NaN codes stay NaN: they only occur in cache slots past a
+// sequence's end, which are clamped away or zeroed before use.
+template <bool HI = false>
 __device__ __forceinline__ unsigned f8x2_to_bf16x2(unsigned w) {
-  const float k = 0x1p120f;
-  const float f0 = __builtin_bit_cast(float, ((w & 0x7Fu) << 20) | ((w & 0x80u) << 24)) * k;
-  const float f1 = __builtin_bit_cast(float, ((w & 0x7F00u) << 12) | ((w & 0x8000u) << 16)) * k;
-  return (__builtin_bit_cast(unsigned, f0) >> 16) | (__builtin_bit_cast(unsigned, f1) & 0xFFFF0000u);
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // ---------------------------------------------------------------------------
@@ -566,12 +561,12 @@ __device__ __forceinline__ void v_words(const typename VRawT<KIND, MD>::T& r, un
     for (int i = 0; i < MD / 2; ++i) out[i] = r[i];
   } else if constexpr (MD == 8) {
     out[0] = f8x2_to_bf16x2(r[0]);
-    out[1] = f8x2_to_bf16x2(r[0] >> 16);
+    out[1] = f8x2_to_bf16x2<true>(r[0]);
     out[2] = f8x2_to_bf16x2(r[1]);
-    out[3] = f8x2_to_bf16x2(r[1] >> 16);
+    out[3] = f8x2_to_bf16x2<true>(r[1]);
   } else {
     out[0] = f8x2_to_bf16x2(r);
-    out[1] = f8x2_to_bf16x2(r >> 16);
+    out[1] = f8x2_to_bf16x2<true>(r);
   }
 }
 
@@ -1286,13 +1281,23 @@ struct Stage {
   KReg kr[KCH];
   u32x4 vf[KIND == KIND_F32 ? VCH : 1];
   typename VRawT<KIND == KIND_F32 ? KIND_BF16 : KIND, MD>::T vraw[KIND == KIND_F32 ? 1 : 4];
+  float ksc, vsc;   // fp8: the staged tile's K and V scales (per-(page, head) mode)
 
   // global -> registers for the given tile.  Thread t stages K chunks
   // c = i * 256 + t (lane c % 64 of operand (mb, ks) = c / 64, a row of the
   // tile: key 16 mb + lane % 16) and V rows 32 ks2 + 16 half + 4 (lane / 16) + j.
-  __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile) {
+  // FAST: `page` is the tile's physical page, from the caller's page window
+  __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, int page) {
     Tile<C::ELT, FAST> t;
-    t.init(p, s, tile);
+    // the tile's scales travel with its data, so the step that uses them
+    // does not wait on a dependent page-table and scale lookup
+    if constexpr (FAST) {
+      t.init_at_page(p, s, tile, page);
+      if constexpr (KIND == KIND_F8) ksc = kscale_at_page<KIND>(p, s, page, &vsc);
+    } else {
+      t.init(p, s, tile);
+      if constexpr (KIND == KIND_F8) ksc = kscale_of<KIND>(p, s, t.J0, &vsc);
+    }
     const int tid = threadIdx.x;
     const int ln = tid & 63, m = ln & 15, hh = ln >> 4;
     const bool full = t.nvalid == kUnitKeys;
@@ -1409,6 +1414,9 @@ struct DirectStage {
 
   // (re)point at sequence s.b, kv head s.g; the page window survives while the
   // sequence stays the same
+  // ELT: bytes per K/V element (the direct loads are bf16; other kinds use
+  // only the page window)
+  template <int ELT = 2>
   __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s) {
     if (s.b == cur_b && s.g == cur_g) return;
     if (s.b != cur_b) pbase = -(1 << 30);
@@ -1418,12 +1426,12 @@ struct DirectStage {
     max_pages = held(p.max_pages);
     num_pages = held(p.num_pages);
     page_mask = held(p.page_size - 1);
-    kbase = wave_uniform(reinterpret_cast<const char*>(p.k) + (int64_t)s.g * p.k_sh * 2);
-    vbase = wave_uniform(reinterpret_cast<const char*>(p.v) + (int64_t)s.g * p.v_sh * 2);
-    ksp = (uint64_t)p.k_sp * 2;
-    vsp = (uint64_t)p.v_sp * 2;
-    kss = (uint32_t)(p.k_ss * 2);
-    vss = (uint32_t)(p.v_ss * 2);
+    kbase = wave_uniform(reinterpret_cast<const char*>(p.k) + (int64_t)s.g * p.k_sh * ELT);
+    vbase = wave_uniform(reinterpret_cast<const char*>(p.v) + (int64_t)s.g * p.v_sh * ELT);
+    ksp = (uint64_t)p.k_sp * ELT;
+    vsp = (uint64_t)p.v_sp * ELT;
+    kss = (uint32_t)(p.k_ss * ELT);
+    vss = (uint32_t)(p.v_ss * ELT);
     bt_row = s.bt_row;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, hh = lane >> 4;
@@ -1562,7 +1570,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   WaveState<KIND, D, NB> st;
   st.init();
   Stage<KIND, D, FAST> stg;
-  if constexpr (DIRECT) ds.init(p, s);             // keeps its page window while the sequence stays
+  stg.ksc = stg.vsc = 1.f;
+  float cur_ksc = 1.f, cur_vsc = 1.f;              // scales of the tile in the current stage
+  if constexpr (FAST) ds.init<C::ELT>(p, s);       // keeps its page window while the sequence stays
 
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
     const int cn = min(kMaskListCap, u1 - c0);
@@ -1574,8 +1584,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       ds.load(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
     } else {
-      stg.load(p, s, tile_of(c0));
+      stg.load(p, s, tile_of(c0), FAST ? ds.page_of_tile(p, tile_of(c0) * kUnitKeys) : -1);
       stg.store(smem, smem + C::K_TILE);
+      cur_ksc = stg.ksc;
+      cur_vsc = stg.vsc;
     }
     __syncthreads();
     // one tile; BUF (a compile-time 0 / 1) selects the stage it reads, so every
@@ -1597,14 +1609,17 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           for (int i = 0; i < 8; ++i) ds.issue(i, nkb, nvb);
         }
       } else if (more) {
-        stg.load(p, s, tile_of(u + 1));
+        stg.load(p, s, tile_of(u + 1), FAST ? ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys) : -1);
       }
       __builtin_amdgcn_sched_barrier(0);
       const int tile = tile_of(u);
       const int J0 = tile * kUnitKeys;
       if (wave_live) {
-        float vsc;
-        const float ksc = kscale_of<KIND>(p, s, J0, &vsc);
+        float vsc = 1.f, ksc = 1.f;
+        if constexpr (KIND == KIND_F8) {
+          ksc = cur_ksc;
+          vsc = cur_vsc;
+        }
         float cs = tp.sm_log2;
         if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
         if (tp.has_bm) {
@@ -1752,6 +1767,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       } else if (more) {
         char* nk = smem + (buf ^ 1) * C::STAGE;
         stg.store(nk, nk + C::K_TILE);
+        cur_ksc = stg.ksc;
+        cur_vsc = stg.vsc;
       }
       __syncthreads();
     };
