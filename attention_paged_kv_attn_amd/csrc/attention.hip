@@ -111,6 +111,16 @@ __device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_qk(long a, long b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
+// fp8, d = 128: one 16x16x128 MFMA over the whole head dim.  A lane's four
+// 16x16x32 K-step operands, concatenated, pair slot for slot with the Q row's
+// four operands concatenated the same way, so the sum runs over all 128 dims.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 cat4(long a0, long a1, long a2, long a3) {
+  return i32x8{(int)a0, (int)(a0 >> 32), (int)a1, (int)(a1 >> 32), (int)a2, (int)(a2 >> 32), (int)a3, (int)(a3 >> 32)};
+}
+__device__ __forceinline__ f32x4 mfma_qk128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);   // E4M3 x E4M3, no block scales
+}
 __device__ __forceinline__ f32x4 mfma_pv(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -838,11 +848,17 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
   f32x4 sc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) sc[mb] = f32x4{0, 0, 0, 0};
+  if constexpr (KIND == KIND_F8 && D == 128) {
+    const i32x8 qc = cat4(qsrc(0, lane), qsrc(1, lane), qsrc(2, lane), qsrc(3, lane));
 #pragma unroll
-  for (int ks = 0; ks < C::KSQ; ++ks) {
-    const typename QKOpT<KIND>::T qb = qsrc(ks, lane);
+    for (int mb = 0; mb < 4; ++mb) sc[mb] = mfma_qk128(cat4(r.kA[mb][0], r.kA[mb][1], r.kA[mb][2], r.kA[mb][3]), qc, sc[mb]);
+  } else {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) sc[mb] = mfma_qk(r.kA[mb][ks], qb, sc[mb]);
+    for (int ks = 0; ks < C::KSQ; ++ks) {
+      const typename QKOpT<KIND>::T qb = qsrc(ks, lane);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sc[mb] = mfma_qk(r.kA[mb][ks], qb, sc[mb]);
+    }
   }
   const TileParams tp = TileParams::of(p);
   const uint64_t lmk = landmark_bits(tp, J0);
@@ -1650,6 +1666,25 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka[i], qB[nb][4 * cc + i], sc[nb][mb]);
             }
+        } else if constexpr (KIND == KIND_F8 && D == 128) {
+          // one 16x16x128 MFMA per (mb, nb); the next mb's four K operands are
+          // read while this mb's MFMAs run
+          i32x8 qc[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) qc[nb] = cat4(qB[nb][0], qB[nb][1], qB[nb][2], qB[nb][3]);
+          auto kread4 = [&](int mb) -> i32x8 {
+            const char* at = kbuf + (mb * 4 * 64 + lane) * 8;
+            return cat4(*reinterpret_cast<const long*>(at), *reinterpret_cast<const long*>(at + 512),
+                        *reinterpret_cast<const long*>(at + 1024), *reinterpret_cast<const long*>(at + 1536));
+          };
+          i32x8 kc = kread4(0);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            const i32x8 ka = kc;
+            if (mb + 1 < 4) kc = kread4(mb + 1);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk128(ka, qc[nb], sc[nb][mb]);
+          }
         } else {
           // K operands stream from LDS KDEP reads ahead of the MFMAs that use
           // them (the schedule groups below keep that order), so the reads'
