@@ -1427,6 +1427,7 @@ struct DirectStage {
   // per lane: constant parts of the load offsets
   uint32_t k_col, v_col;      // byte column within a row
   int k_row0, v_row0;         // row of load i = 0 (K: + 16 i, V: + 16 i)
+  uint32_t k_lane, v_lane;    // byte offsets of the lane's rows for load i = 0
 
   // (re)point at sequence s.b, kv head s.g; the page window survives while the
   // sequence stays the same
@@ -1456,6 +1457,8 @@ struct DirectStage {
     const int rl = lane >> 4, sl = lane & 15;
     v_row0 = 4 * wave + rl;                             // row 16 i + 4 wave + rl
     v_col = 16u * (sl ^ (2 * (v_row0 & 7)));             // swizzled 16-byte column (row & 7 is i-invariant)
+    k_lane = (uint32_t)k_row0 * kss + k_col;
+    v_lane = (uint32_t)v_row0 * vss + v_col;
   }
 
   __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
@@ -1484,7 +1487,7 @@ struct DirectStage {
   // last key (finite values; their scores are masked).
   const char* pk_b;
   const char* pv_b;
-  int plim;
+  int pnvalid;
   // The addresses of one tile's DMAs; issue(i) then starts DMA i of 8 (K rows
   // for i < 4, V rows after).  A DMA holds its wave until the address unit
   // takes it, so the tile loop spreads the eight over its QK MFMAs.
@@ -1494,12 +1497,27 @@ struct DirectStage {
     const uint32_t slot = (uint32_t)(J0 & page_mask);
     pk_b = wave_uniform(kbase + page * ksp + slot * kss);
     pv_b = wave_uniform(vbase + page * vsp + slot * vss);
-    plim = min(kUnitKeys, s.ctx - J0) - 1;
+    pnvalid = min(kUnitKeys, s.ctx - J0);
   }
+  // The tile lies in one page, so rows past the sequence end are still cache
+  // memory: they are read as they are (their scores are masked by select)
+  // and their V rows are zeroed once landed (zero_tail), so no garbage reaches
+  // P V.  Row 16 i of a load moves the scalar base only.
   __device__ __forceinline__ void issue(int i, char* kbuf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (i < 4) gload16_lds(pk_b, kbuf + 1024 * (4 * i + wave), (uint32_t)min(k_row0 + 16 * i, plim) * kss + k_col, 0u);
-    else gload16_lds(pv_b, vbuf + 1024 * (4 * (i - 4) + wave), (uint32_t)min(v_row0 + 16 * (i - 4), plim) * vss + v_col, 0u);
+    if (i < 4) gload16_lds(wave_uniform(pk_b + (uint32_t)(16 * i) * kss), kbuf + 1024 * (4 * i + wave), k_lane, 0u);
+    else gload16_lds(wave_uniform(pv_b + (uint32_t)(16 * (i - 4)) * vss), vbuf + 1024 * (4 * (i - 4) + wave), v_lane, 0u);
+  }
+  // after this wave's DMAs into vbuf have landed (vmcnt): zero the V rows it
+  // loaded past the sequence end; every lane clears the 16 bytes it wrote
+  __device__ __forceinline__ void zero_tail(char* vbuf) {
+    if (pnvalid >= kUnitKeys) return;                     // uniform: only a sequence's last tile
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (v_row0 + 16 * i >= pnvalid)
+        *reinterpret_cast<u32x4*>(vbuf + 1024 * (4 * i + wave) + 16 * lane) = u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
     prep(p, s, tile);
@@ -1599,6 +1617,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     if constexpr (DIRECT) {
       ds.load(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
+      ds.zero_tail(vstage<true>(0));
     } else {
       stg.load(p, s, tile_of(c0), FAST ? ds.page_of_tile(p, tile_of(c0) * kUnitKeys) : -1);
       stg.store(smem, smem + C::K_TILE);
@@ -1799,6 +1818,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (DIRECT) {
         wait_vmem();
+        ds.zero_tail(nvb);
       } else if (more) {
         char* nk = smem + (buf ^ 1) * C::STAGE;
         stg.store(nk, nk + C::K_TILE);
