@@ -50,7 +50,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh) 
 
 // Steps 0 and 1 (one workgroup): metadata checks, then the first Q-block of
 // every sequence.  Returns n_qb, or -1 after writing an error header.
-__device__ int assign_sequences(const KParams& p, int* sh, int* err) {
+// The single-workgroup path keeps the per-sequence bases and the per-Q-block
+// counts in LDS when they fit, so that the binary searches and the prefix pass
+// read LDS instead of a chain of global loads.
+constexpr int kSeqLds = 2048;      // sequences + 1
+constexpr int kQbLds = 8192;       // Q-blocks + 1
+
+__device__ int assign_sequences(const KParams& p, int* sh, int* err, int* base_lds) {
   const int tid = threadIdx.x;
   if (tid == 0) *err = E_NONE;
   __syncthreads();
@@ -82,10 +88,16 @@ __device__ int assign_sequences(const KParams& p, int* sh, int* err) {
       nqb *= p.Hkv;
     }
     const int ex = block_exclusive_scan(nqb, &tot, sh);
-    if (b < p.B) p.seq_qb_base[b] = carry + ex;
+    if (b < p.B) {
+      p.seq_qb_base[b] = carry + ex;
+      if (base_lds) base_lds[b] = carry + ex;
+    }
     carry += tot;
   }
-  if (tid == 0) p.seq_qb_base[p.B] = carry;
+  if (tid == 0) {
+    p.seq_qb_base[p.B] = carry;
+    if (base_lds) base_lds[p.B] = carry;
+  }
   __syncthreads();
   return carry;
 }
@@ -95,16 +107,17 @@ struct QbTiles {
   int b, g, pos_lo, pos_hi, t_lo, t_hi;
   bool any;
 };
-__device__ __forceinline__ QbTiles assign_descriptor(const KParams& p, int q) {
+// `base`: the per-sequence first Q-block (LDS copy or the workspace array)
+__device__ __forceinline__ QbTiles assign_descriptor(const KParams& p, int q, const int* base) {
   int lo = 0, hi = p.B - 1;                        // last b with base[b] <= q
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.seq_qb_base[mid] <= q) lo = mid; else hi = mid - 1;
+    if (base[mid] <= q) lo = mid; else hi = mid - 1;
   }
   const int b = lo;
   const int nt_large = kLargeRows / p.G;
-  const int per_g = (p.seq_qb_base[b + 1] - p.seq_qb_base[b]) / p.Hkv;
-  const int rem = q - p.seq_qb_base[b];
+  const int per_g = (base[b + 1] - base[b]) / p.Hkv;
+  const int rem = q - base[b];
   const int g = rem / per_g, t = rem % per_g;
   const int q0 = p.qsl[b], ql = p.qsl[b + 1] - q0, ctx = p.seq_lens[b];
   const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
@@ -124,18 +137,27 @@ __device__ __forceinline__ QbTiles assign_descriptor(const KParams& p, int q) {
 }
 
 // Steps 3 and 4 (one workgroup): unit prefix, L, splits, combine list, slots, header.
-__device__ void assign_splits(const KParams& p, int n_qb, int* sh) {
+// `pre`: LDS copy of unit_prefix (counts parked at [q + 1] on entry), or null
+// to work on the workspace array
+__device__ void assign_splits(const KParams& p, int n_qb, int* sh, int* pre) {
   const int tid = threadIdx.x;
+  int* up = pre ? pre : p.unit_prefix;
   // 3. unit prefix
   int carry = 0, tot;
   for (int c0 = 0; c0 < n_qb; c0 += kAssignThreads) {
     const int q = c0 + tid;
-    const int n = q < n_qb ? p.unit_prefix[q + 1] : 0;
+    const int n = q < n_qb ? up[q + 1] : 0;
     const int ex = block_exclusive_scan(n, &tot, sh);
-    if (q < n_qb) p.unit_prefix[q + 1] = carry + ex + n;
+    if (q < n_qb) {
+      up[q + 1] = carry + ex + n;
+      if (pre) p.unit_prefix[q + 1] = carry + ex + n;
+    }
     carry += tot;
   }
-  if (tid == 0) p.unit_prefix[0] = 0;
+  if (tid == 0) {
+    p.unit_prefix[0] = 0;
+    if (pre) pre[0] = 0;
+  }
   const int U = carry;
   const int L = p.force_L > 0 ? p.force_L : max(p.L_min, (U + p.P - 1) / p.P);
   __syncthreads();
@@ -146,7 +168,7 @@ __device__ void assign_splits(const KParams& p, int n_qb, int* sh) {
     const int q = c0 + tid;
     int ns = 1;
     if (q < n_qb) {
-      const int S = p.unit_prefix[q], n = p.unit_prefix[q + 1] - S;
+      const int S = up[q], n = up[q + 1] - S;
       ns = n == 0 ? 0 : (S + n - 1) / L - S / L + 1;
       p.n_splits[q] = ns;
     }
@@ -180,15 +202,21 @@ __device__ void assign_splits(const KParams& p, int n_qb, int* sh) {
 __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
   __shared__ int sh[kAssignThreads / 64 + 1];
   __shared__ int err;
-  const int n_qb = assign_sequences(p, sh, &err);
+  __shared__ int base_lds[kSeqLds];
+  __shared__ int pre_lds[kQbLds];
+  int* bl = p.B + 1 <= kSeqLds ? base_lds : nullptr;
+  const int n_qb = assign_sequences(p, sh, &err, bl);
   if (n_qb < 0) return;
-  // 2. descriptors and unit counts (counts parked in unit_prefix[q + 1])
+  int* pl = n_qb + 1 <= kQbLds ? pre_lds : nullptr;
+  // 2. descriptors and unit counts (counts parked at [q + 1])
   for (int q = threadIdx.x; q < n_qb; q += kAssignThreads) {
-    const QbTiles r = assign_descriptor(p, q);
-    p.unit_prefix[q + 1] = r.any ? r.t_hi - r.t_lo + 1 : 0;
+    const QbTiles r = assign_descriptor(p, q, bl ? bl : p.seq_qb_base);
+    const int n = r.any ? r.t_hi - r.t_lo + 1 : 0;
+    if (pl) pl[q + 1] = n;
+    else p.unit_prefix[q + 1] = n;
   }
   __syncthreads();
-  assign_splits(p, n_qb, sh);
+  assign_splits(p, n_qb, sh, pl);
 }
 
 // With a block mask the unit counts are the expensive part, so they get a
@@ -199,7 +227,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
 __global__ __launch_bounds__(kAssignThreads) void assign_begin_kernel(KParams p) {
   __shared__ int sh[kAssignThreads / 64 + 1];
   __shared__ int err;
-  const int n_qb = assign_sequences(p, sh, &err);
+  const int n_qb = assign_sequences(p, sh, &err, nullptr);
   if (n_qb >= 0 && threadIdx.x == 0) p.hdr[H_ERROR] = E_NONE;
 }
 
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(kCountThreads) void assign_count_kernel(KParams p) 
   const int upt = p.bm_tile / kUnitKeys;
   for (int q = blockIdx.x * waves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); q < n_qb; q += gridDim.x * waves) {
     QbTiles r;
-    if (lane == 0) r = assign_descriptor(p, q);
+    if (lane == 0) r = assign_descriptor(p, q, p.seq_qb_base);
     r.b = __shfl(r.b, 0);
     r.g = __shfl(r.g, 0);
     r.pos_lo = __shfl(r.pos_lo, 0);
@@ -245,7 +273,7 @@ __global__ __launch_bounds__(kCountThreads) void assign_count_kernel(KParams p) 
 __global__ __launch_bounds__(kAssignThreads) void assign_end_kernel(KParams p) {
   __shared__ int sh[kAssignThreads / 64 + 1];
   if (p.hdr[H_ERROR] != E_NONE) return;
-  assign_splits(p, p.seq_qb_base[p.B], sh);
+  assign_splits(p, p.seq_qb_base[p.B], sh, nullptr);
 }
 
 hipError_t launch_assign(const KParams& p, hipStream_t stream) {
