@@ -112,8 +112,8 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
                 page_size: int, ctx, q_len, kv_layout: str = "NHD", num_pages: Optional[int] = None,
                 q_rng: Optional[np.random.Generator] = None, q_gain: float = 1.0,
                 identity_pages: bool = False, poison: bool = True, keep_dense: bool = False,
-                quant_mode: Optional[str] = None, softmax_scale: Optional[float] = None,
-                causal: bool = True, window: int = 0, window_expand_to_chunk: bool = True,
+                quant_mode: Optional[str] = None, q_quant: str = "tensor",
+                softmax_scale: Optional[float] = None, causal: bool = True, window: int = 0, window_expand_to_chunk: bool = True,
                 landmark_chunk: int = 0, block_mask_skip: Optional[float] = None,
                 block_mask_tile: int = 128, out_heads_major: bool = False) -> PagedBatch:
     """Lay out one batch.  `ctx` and `q_len` (per sequence) must already be drawn."""
@@ -154,7 +154,15 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
         # scales need every value first: draw all K, then all V
         ks = [torch.randn((c, Hkv, d), generator=k_gen).numpy() for c in ctx]
         vs = [torch.randn((c, Hkv, d), generator=v_gen).numpy() for c in ctx]
-        q_s = _f8_scale(float(np.abs(qs).max()) if qs.size else 0.0)
+        if q_quant == "tensor":
+            q_s = np.float32(_f8_scale(float(np.abs(qs).max()) if qs.size else 0.0))
+        elif q_quant == "token_head":
+            # one scale per (query token, query head): its own amax over d
+            amax = np.abs(qs).max(axis=2) if qs.size else np.zeros(qs.shape[:2], np.float32)
+            q_s = np.vectorize(lambda a: _f8_scale(float(a)), otypes=[np.float32])(amax)
+            q_s = q_s.reshape(qs.shape[:2]).astype(np.float32)
+        else:
+            raise ValueError("q_quant must be 'tensor' or 'token_head'")
         if quant_mode == "tensor":
             k_s = _f8_scale(max((float(np.abs(k).max()) for k in ks if k.size), default=0.0))
             v_s = _f8_scale(max((float(np.abs(v).max()) for v in vs if v.size), default=0.0))
@@ -169,11 +177,14 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
                     for arr, sc in ((ks[b], k_sc), (vs[b], v_sc)):
                         amax = np.abs(arr[sl]).max(axis=(0, 2))
                         sc[bt[b, p]] = [_f8_scale(float(a)) for a in amax]
-        scales = {"mode": quant_mode,
-                  "q": torch.tensor([q_s], dtype=torch.float32),
+        scales = {"mode": quant_mode, "q_mode": q_quant,
+                  "q": torch.from_numpy(np.atleast_1d(q_s).astype(np.float32).copy()),
                   "k": torch.from_numpy(np.atleast_1d(k_sc).astype(np.float32).copy()),
                   "v": torch.from_numpy(np.atleast_1d(v_sc).astype(np.float32).copy())}
-        q_t = _cast(qs, kind, q_s)
+        if q_quant == "tensor":
+            q_t = _cast(qs, kind, float(q_s))
+        else:
+            q_t = _cast(qs / q_s[:, :, None], kind)
     else:
         q_t = _cast(qs, kind)
 
@@ -271,9 +282,12 @@ def decode_ctx_lengths(rng, batch: int, lo: int, hi: int) -> np.ndarray:
 
 def splitk_decode(q_len=1, kv_layout: str = "NHD", seed: int = 2, batch: int = 64,
                   ctx_lo: int = 128, ctx_hi: int = 32768, poison: bool = True,
-                  q_gain: float = 1.0, keep_dense: bool = False) -> PagedBatch:
-    """bf16 Llama-3.1-8B attention shape, log-uniform contexts 128..32768,
-    64-token pages, q_len in {1, 2, 4} (an int) or a per-sequence list (mixed MTP)."""
+                  q_gain: float = 1.0, keep_dense: bool = False, kind: str = "bf16",
+                  quant_mode: str = "tensor", q_quant: str = "token_head") -> PagedBatch:
+    """Llama-3.1-8B attention shape, log-uniform contexts 128..32768,
+    64-token pages, q_len in {1, 2, 4} (an int) or a per-sequence list (mixed MTP).
+    bf16, or e4m3 (K/V scales per `quant_mode`, Q scales per `q_quant`: the
+    decode variant scales Q per (token, head) and K/V per tensor)."""
     rng = np.random.default_rng(seed)
     ctx = decode_ctx_lengths(rng, batch, ctx_lo, ctx_hi)
     if isinstance(q_len, (list, tuple, np.ndarray)):
@@ -282,10 +296,13 @@ def splitk_decode(q_len=1, kv_layout: str = "NHD", seed: int = 2, batch: int = 6
     else:
         ql = [int(q_len)] * batch
         q_seed = 200 + int(q_len)
-    return build_batch(rng, name=f"splitk_decode_q{q_len if isinstance(q_len, int) else 'mix'}_{kv_layout}",
-                       kind="bf16", Hq=32, Hkv=8, d=128, page_size=64, ctx=ctx, q_len=ql,
+    tag = "" if kind == "bf16" else f"_{kind}_{q_quant}_{quant_mode}"
+    return build_batch(rng, name=f"splitk_decode_q{q_len if isinstance(q_len, int) else 'mix'}_{kv_layout}{tag}",
+                       kind=kind, Hq=32, Hkv=8, d=128, page_size=64, ctx=ctx, q_len=ql,
                        kv_layout=kv_layout, q_rng=np.random.default_rng(q_seed), q_gain=q_gain,
-                       poison=poison, keep_dense=keep_dense)
+                       poison=poison, keep_dense=keep_dense,
+                       quant_mode=quant_mode if kind == "e4m3" else None,
+                       q_quant=q_quant if kind == "e4m3" else "tensor")
 
 
 def hybrid_chunked(seed: int = 3, chunk_last: bool = False, poison: bool = True,

@@ -30,7 +30,9 @@ What is computed, for every sequence b, query token i and query head h:
   stage 1).  A row with no visible key has O = 0 and LSE = -inf.
 * stored values are upcast exactly: f32 as is, bf16 by widening its bits,
   e4m3 through the E4M3FN table times its scale (per tensor, or per
-  (physical page, kv head) for K and V).  The fp32 softmax scale is used as
+  (physical page, kv head) for K and V; Q per tensor, or per (query token,
+  query head) as in the FP8 decode quantisation path of "Triton-TLE rewrite
+  of Tencent HPC-Ops Attention", §3 Dynamic Decode, its FP8 results).  The fp32 softmax scale is used as
   passed, widened to float64.
 
 Everything is float64.  Query rows are processed in blocks of row_block
@@ -113,7 +115,8 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
     block_table int [B, max_pages]; seq_lens int [B]; query_start_loc int [B+1]
     block_mask  uint8 [B, H_m, n_q_tiles, n_k_tiles] with H_m in {1, Hq}, or None
     scales   for kind "e4m3": {"mode": "tensor"|"page_head", "q": float,
-             "k": float or [num_pages, Hkv], "v": same}
+             "k": float or [num_pages, Hkv], "v": same}, and optionally
+             "q_mode": "token_head" with "q" a [total_q, Hq] array
     key_range   optional int [B, 2]: only keys lo <= j < hi count (split reference)
     rows     optional boolean [total_q]: compute only these query rows
              (others are left as NaN) — used to evaluate sampled outputs.
@@ -137,9 +140,9 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
     if kind == "e4m3":
         if scales is None:
             raise ValueError("e4m3 inputs need scales")
-        q_scale = float(np.float32(scales["q"]))
+        q_scale = _q_scale(scales, total_q, Hq)
     else:
-        q_scale = 1.0
+        q_scale = None
 
     O = np.full((total_q, Hq, d), np.nan)
     LSE = np.full((total_q, Hq), np.nan)
@@ -169,7 +172,10 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
                 hi = min(ctx, key_hi, int(pos.max()) + 1 if causal else ctx)
                 lo = max(key_lo, int(window_left(pos, window, window_expand_to_chunk,
                                                  landmark_chunk).min()) if window > 0 else 0)
-                qhat = upcast(q[t, g * G:(g + 1) * G, :], kind) * q_scale      # [n, G, d]
+                qhat = upcast(q[t, g * G:(g + 1) * G, :], kind)                # [n, G, d]
+                if q_scale is not None:
+                    qhat = qhat * (q_scale if np.isscalar(q_scale)
+                                   else q_scale[t, g * G:(g + 1) * G, None])
                 if hi <= lo:
                     O[t, g * G:(g + 1) * G, :] = 0.0
                     LSE[t, g * G:(g + 1) * G] = -math.inf
@@ -196,6 +202,19 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
                     O[t, h, :] = o
                     LSE[t, h] = lse
     return O, LSE
+
+
+def _q_scale(scales, total_q, Hq):
+    """The Q dequantisation scale: one float, or per (query token, query head)."""
+    mode = scales.get("q_mode", "tensor")
+    if mode == "tensor":
+        return float(np.float32(scales["q"]))
+    if mode == "token_head":
+        s = np.asarray(scales["q"], dtype=np.float32).astype(np.float64)
+        if s.shape != (total_q, Hq):
+            raise ValueError("per-(token, head) Q scales must be [total_q, Hq]")
+        return s
+    raise ValueError(mode)
 
 
 def _kv_scale(scales, which, pages, g):

@@ -20,7 +20,9 @@ def oracle_scales(batch):
     v = s["v"].cpu().numpy()
     if s["mode"] == "tensor":
         k, v = float(k[0]), float(v[0])
-    return {"mode": s["mode"], "q": float(s["q"].cpu()[0]), "k": k, "v": v}
+    q_mode = s.get("q_mode", "tensor")
+    q = float(s["q"].cpu()[0]) if q_mode == "tensor" else s["q"].cpu().numpy()
+    return {"mode": s["mode"], "q_mode": q_mode, "q": q, "k": k, "v": v}
 
 
 def run_oracle(batch, **overrides):

@@ -12,8 +12,17 @@ from oracle.attention import paged_attention, visible
 from tests.oracle_helpers import dequant64, run_oracle, stored_np
 
 
+def _q_scale64(batch):
+    """The Q scale as a float or a [total_q, Hq, 1] array, widened by torch."""
+    if batch.scales is None:
+        return None
+    if batch.scales.get("q_mode", "tensor") == "tensor":
+        return float(batch.scales["q"][0])
+    return batch.scales["q"].to(torch.float64).numpy()[:, :, None]
+
+
 def _dense_lists(batch, scales_per_seq=None):
-    q = dequant64(batch.q, None if batch.scales is None else float(batch.scales["q"][0])).tolist()
+    q = dequant64(batch.q, _q_scale64(batch)).tolist()
     ks, vs = [], []
     for b, (k, v) in enumerate(zip(batch.dense_k, batch.dense_v)):
         if batch.scales is None:
@@ -60,15 +69,42 @@ def test_brute_force_tiny_hybrid():
 
 @pytest.mark.parametrize("mode", ["tensor", "page_head"])
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
-def test_brute_force_fp8(mode, layout):
+@pytest.mark.parametrize("q_quant", ["tensor", "token_head"])
+def test_brute_force_fp8(mode, layout, q_quant):
     rng = np.random.default_rng(41)
     b = W.build_batch(rng, name="tiny_fp8", kind="e4m3", Hq=4, Hkv=2, d=32, page_size=16,
                       ctx=[40, 70], q_len=[1, 20], num_pages=12, quant_mode=mode, keep_dense=True,
-                      kv_layout=layout)
+                      kv_layout=layout, q_quant=q_quant)
     O, L = run_oracle(b)
     Ob, Lb = _brute(b)
     assert np.abs(O - Ob).max() <= 1e-12
     assert np.abs(L - Lb).max() <= 1e-12
+
+
+def test_token_head_q_scale_reduces_to_per_tensor():
+    """Per-(token, head) Q scales that are all equal give the per-tensor result
+    bit for bit; scaling one (token, head) entry changes that row only."""
+    rng = np.random.default_rng(43)
+    b = W.build_batch(rng, name="tiny_fp8_q", kind="e4m3", Hq=8, Hkv=2, d=32, page_size=16,
+                      ctx=[33, 90, 17], q_len=[1, 4, 2], num_pages=16, quant_mode="tensor",
+                      q_quant="tensor")
+    c = float(b.scales["q"][0])
+    total_q, Hq = b.q.shape[:2]
+    O1, L1 = run_oracle(b)
+    sc = {"mode": "tensor", "q_mode": "token_head", "q": np.full((total_q, Hq), c, np.float32),
+          "k": float(b.scales["k"][0]), "v": float(b.scales["v"][0])}
+    O2, L2 = run_oracle(b, scales=sc)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    sc["q"] = sc["q"].copy()
+    sc["q"][3, 5] *= 4.0
+    O3, L3 = run_oracle(b, scales=sc)
+    changed = np.zeros((total_q, Hq), dtype=bool)
+    changed[3, 5] = True
+    assert np.array_equal(O3[~changed], O1[~changed]) and np.array_equal(L3[~changed], L1[~changed])
+    assert not np.allclose(O3[3, 5], O1[3, 5])
+    # a Q scale of c * 4 on one row is the same as a softmax scale four times as large there
+    O4, L4 = run_oracle(b, softmax_scale=4.0 * b.softmax_scale)
+    assert np.abs(O3[3, 5] - O4[3, 5]).max() <= 1e-12 and abs(L3[3, 5] - L4[3, 5]) <= 1e-12
 
 
 def _sdpa_check(batch):
@@ -76,8 +112,7 @@ def _sdpa_check(batch):
     O, _ = run_oracle(batch)
     G = batch.num_q_heads // batch.num_kv_heads
     qsl = batch.query_start_loc.tolist()
-    qs = None if batch.scales is None else float(batch.scales["q"][0])
-    q64 = torch.from_numpy(dequant64(batch.q, qs))
+    q64 = torch.from_numpy(dequant64(batch.q, _q_scale64(batch)))
     worst = 0.0
     for b, ctx in enumerate(batch.seq_lens.tolist()):
         q0, q1 = qsl[b], qsl[b + 1]
