@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 PA_F32, PA_BF16, PA_F8E4M3, PA_U8 = range(4)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_PAGE_HEAD = range(3)
+PA_SCALE_Q_PER_TOKEN_HEAD = 4
 
 EXPORTS = ("paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_workspace_layout",
            "paged_attn_validate_host", "paged_attn_device_info", "paged_attn_status_string",
@@ -255,6 +256,13 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     if scales is not None:
         sc = pa_scales()
         sc.mode = {"tensor": PA_SCALE_PER_TENSOR, "page_head": PA_SCALE_PER_PAGE_HEAD}[scales["mode"]]
+        if scales.get("q_mode", "tensor") == "token_head":
+            qs = scales["q"]
+            if qs.dtype != torch.float32 or not qs.is_contiguous() or qs.numel() != total_q * Hq:
+                raise ValueError("per-(token, head) Q scales must be contiguous fp32 [total_q, Hq]")
+            sc.mode |= PA_SCALE_Q_PER_TOKEN_HEAD
+        elif scales.get("q_mode", "tensor") != "tensor":
+            raise ValueError("q_mode must be 'tensor' or 'token_head'")
         sc.q_scale, sc.k_scale, sc.v_scale = (scales["q"].data_ptr(), scales["k"].data_ptr(),
                                               scales["v"].data_ptr())
     if stream is None:

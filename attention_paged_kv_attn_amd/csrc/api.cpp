@@ -265,8 +265,9 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   int scale_mode = 0;
   if (dt == PA_F8E4M3) {
     if (!scales || !scales->q_scale || !scales->k_scale || !scales->v_scale) return PA_ERR_INVALID_ARG;
-    if (scales->mode != PA_SCALE_PER_TENSOR && scales->mode != PA_SCALE_PER_PAGE_HEAD) return PA_ERR_INVALID_ARG;
-    if (scales->mode == PA_SCALE_PER_PAGE_HEAD && P.page_size < 64) return PA_ERR_UNSUPPORTED;
+    const int kv_mode = scales->mode & ~PA_SCALE_Q_PER_TOKEN_HEAD;
+    if (kv_mode != PA_SCALE_PER_TENSOR && kv_mode != PA_SCALE_PER_PAGE_HEAD) return PA_ERR_INVALID_ARG;
+    if (kv_mode == PA_SCALE_PER_PAGE_HEAD && P.page_size < 64) return PA_ERR_UNSUPPORTED;
     scale_mode = scales->mode;
   }
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;

@@ -322,10 +322,18 @@ __device__ __forceinline__ float kscale_at_page(const KParams& p, const SeqCtx& 
     *vsc = 1.f;
     return 1.f;
   } else {
-    const int i = p.scale_mode == 2 ? page * p.Hkv + s.g : 0;
+    const int i = (p.scale_mode & 3) == 2 ? page * p.Hkv + s.g : 0;
     *vsc = p.v_scale[i];
     return p.k_scale[i];
   }
+}
+
+// Q scale of one query row: per tensor, or per (query token, query head)
+// from a [total_q, Hq] array.
+template <int KIND>
+__device__ __forceinline__ float qscale_of(const KParams& p, int tok, int head) {
+  if constexpr (KIND != KIND_F8) return 1.f;
+  else return (p.scale_mode & 4) ? p.q_scale[(int64_t)tok * p.Hq + head] : p.q_scale[0];
 }
 
 template <int KIND>
@@ -334,7 +342,7 @@ __device__ __forceinline__ float kscale_of(const KParams& p, const SeqCtx& s, in
     *vsc = 1.f;
     return 1.f;
   } else {
-    if (p.scale_mode == 2) {              // per (physical page, kv head); page_size >= 64
+    if ((p.scale_mode & 3) == 2) {        // per (physical page, kv head); page_size >= 64
       const int page = page_of(p, s, key);
       *vsc = p.v_scale[page * p.Hkv + s.g];
       return p.k_scale[page * p.Hkv + s.g];
@@ -387,6 +395,7 @@ __device__ __forceinline__ void load_qk_row(const char* row, int h,
 struct RowMask {
   int pos, left;    // causal bound and window start of this lane's row
   bool bit;         // block-mask bit of (row's query tile, the unit's key tile)
+  float qs;         // FP8 Q scale of this lane's row (1 otherwise)
 };
 
 // The mask and scale parameters a tile loop tests on every tile.
@@ -864,7 +873,7 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
   const uint64_t lmk = landmark_bits(tp, J0);
   const bool full = unit_is_full(tp, J0, tc.nvalid, pos_min, left_max);
   float cs = tp.sm_log2;
-  if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
+  if constexpr (KIND == KIND_F8) cs *= rm.qs * ksc;
   if (!full) {
     ElemMask em;
     em.init(tp, rm, J0, tc.nvalid, lmk, h);
@@ -949,6 +958,7 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
   rm.pos = x.ctx - x.ql + x.t0 + r / p.G;
   rm.left = p.window > 0 ? window_left(p, rm.pos) : 0;
   rm.bit = true;
+  rm.qs = qscale_of<KIND>(p, tok, head);
   const int pos_min = x.pos_lo;
   const int left_max = p.window > 0 ? window_left(p, x.pos_hi) : 0;
   const int bm_head = p.bm && p.bm_heads != 1 ? head : 0;
@@ -1202,6 +1212,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
         rm.pos = cx.ctx - cx.ql + cx.t0 + r / p.G;
         rm.left = p.window > 0 ? window_left(p, rm.pos) : 0;
         rm.bit = true;
+        rm.qs = qscale_of<KIND>(p, cx.q0 + cx.t0 + r / p.G, cx.g * p.G + r % p.G);
         pos_min = cx.pos_lo;
         left_max = p.window > 0 ? window_left(p, cx.pos_hi) : 0;
       }
@@ -1590,6 +1601,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     rm[nb].pos = x.ctx - x.ql + x.t0 + rowi[nb] / p.G;
     rm[nb].left = p.window > 0 ? window_left(p, rm[nb].pos) : 0;
     rm[nb].bit = true;
+    rm[nb].qs = qscale_of<KIND>(p, tok, head);
     bm_head[nb] = p.bm && p.bm_heads != 1 ? head : 0;
   }
   if (wave_live) {
@@ -1656,7 +1668,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           vsc = cur_vsc;
         }
         float cs = tp.sm_log2;
-        if constexpr (KIND == KIND_F8) cs *= p.q_scale[0] * ksc;
+        if constexpr (KIND == KIND_F8) cs *= ksc;
         if (tp.has_bm) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
@@ -1755,7 +1767,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           }
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], cs);
+        for (int nb = 0; nb < NB; ++nb)
+          softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], KIND == KIND_F8 ? cs * rm[nb].qs : cs);
         __builtin_amdgcn_s_setprio(0);
         // O^T += V^T P^T
         if constexpr (KIND == KIND_F32) {

@@ -45,7 +45,7 @@ struct KParams {
   const uint8_t* bm; int64_t bm_sb, bm_sh, bm_sq, bm_sk;
   int32_t bm_heads, bm_nq, bm_nk, bm_tile;
   const float* q_scale; const float* k_scale; const float* v_scale;
-  int32_t scale_mode;
+  int32_t scale_mode;   // bits 0-1: K/V scale kind (1 per tensor, 2 per (page, kv head)); bit 2: Q per (token, head)
   // sizes
   int32_t B, Hq, Hkv, G, D, page_size, page_shift, num_pages, total_q, max_pages;
   // scores and masks

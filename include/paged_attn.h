@@ -77,12 +77,19 @@ typedef struct pa_tensor {
 typedef enum pa_scale_mode {
   PA_SCALE_NONE = 0,
   PA_SCALE_PER_TENSOR = 1,      /* q_scale, k_scale, v_scale: one fp32 each */
-  PA_SCALE_PER_PAGE_HEAD = 2    /* q_scale: one fp32; k_scale, v_scale: fp32 [num_pages, Hkv] */
+  PA_SCALE_PER_PAGE_HEAD = 2,   /* q_scale: one fp32; k_scale, v_scale: fp32 [num_pages, Hkv] */
+  /* A flag OR'd into either mode above: q_scale is fp32 [total_q, Hq],
+   * contiguous, one scale per (query token, query head) — the FP8 decode
+   * quantisation of "Triton-TLE rewrite of Tencent HPC-Ops Attention", §3
+   * Dynamic Decode (Q per token and head, K/V per tensor). */
+  PA_SCALE_Q_PER_TOKEN_HEAD = 4
 } pa_scale_mode;
 
 /* FP8 dequantisation scales (device pointers, so a call never reads them on
  * the host and stays capturable in a HIP graph).  Value = e4m3(x) * scale;
- * every scale must be finite and > 0.
+ * every scale must be finite and > 0.  mode = PA_SCALE_PER_TENSOR or
+ * PA_SCALE_PER_PAGE_HEAD, optionally | PA_SCALE_Q_PER_TOKEN_HEAD; any other
+ * value is PA_ERR_INVALID_ARG.
  * Required when Q/K/V are PA_F8E4M3, ignored otherwise. */
 typedef struct pa_scales {
   int32_t mode;             /* pa_scale_mode */

@@ -234,6 +234,49 @@ def test_decode_full_size_sampled(q_len, layout):
     compare(b, out, lse, rows=rows)
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("q_len", [1, 2, 4])
+@pytest.mark.parametrize("q_quant", ["token_head", "tensor"])
+def test_fp8_decode_reduced(q_quant, q_len, layout):
+    b = W.splitk_decode(q_len=q_len, kv_layout=layout, batch=12, ctx_lo=100, ctx_hi=6000, kind="e4m3",
+                        q_quant=q_quant)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+def test_fp8_decode_page_head_kv_mixed_mtp():
+    b = W.splitk_decode(q_len=[1, 2, 4, 3, 1, 4, 2, 1], batch=8, ctx_lo=64, ctx_hi=5000, kind="e4m3",
+                        quant_mode="page_head", q_quant="token_head", q_gain=4.0)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+@pytest.mark.parametrize("q_len,layout", [(1, "HND"), (4, "NHD")])
+def test_fp8_decode_full_size_sampled(q_len, layout):
+    b = W.splitk_decode(q_len=q_len, kv_layout=layout, kind="e4m3")
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    ctx = b.seq_lens.numpy()
+    seqs = {int(ctx.argmin()), int(ctx.argmax())} | set(np.random.default_rng(2).choice(64, 4).tolist())
+    rows = np.zeros(b.total_q, bool)
+    qsl = b.query_start_loc.numpy()
+    for s in seqs:
+        rows[qsl[s]:qsl[s + 1]] = True
+    compare(b, out, lse, rows=rows)
+
+
+def test_fp8_prefill_token_head_q():
+    """Per-(token, head) Q scales on the prefill path (two row blocks per lane)."""
+    rng = np.random.default_rng(17)
+    b = W.build_batch(rng, name="prefill_fp8_qtok", kind="e4m3", Hq=32, Hkv=8, d=128, page_size=64,
+                      ctx=[700, 1100], q_len=[700, 300], quant_mode="page_head", q_quant="token_head")
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
 @pytest.mark.parametrize("chunk_last", [False, True])
 def test_hybrid_reduced(chunk_last):
     b = W.hybrid_chunked(batch=16, chunk=512, history=1500, dec_lo=500, dec_hi=4000, chunk_last=chunk_last)
