@@ -691,7 +691,9 @@ __device__ void build_tile_list(const KParams& p, const QBlock& x, int t_lo, int
 // pattern, one tile in flight per wave sustains ~6.2 TB/s while also
 // prefetching the next tile during compute drops to ~3.7 TB/s (the extra
 // outstanding requests congest the memory system); only the next tile's page
-// number is fetched ahead (a scalar load).
+// number is fetched ahead (a scalar load).  An fp8 tile is 16 KiB: there the
+// next tile's K is issued right after this tile's QK and its V right after
+// this tile's PV, which keeps at most one bf16 tile's worth outstanding.
 // ---------------------------------------------------------------------------
 template <int KIND, int D>
 struct SmallRegs {
@@ -835,13 +837,14 @@ struct QFromRegs {
   __device__ __forceinline__ typename QKOpT<KIND>::T operator()(int ks, int) const { return q[ks]; }
 };
 
+// Scores of one tile, S^T = K Q^T, masked and passed through the online
+// softmax: leaves P (unnormalised probabilities) in sc; returns the tile's V scale.
 template <int KIND, int D, bool FAST, class QSrc>
-__device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s, const QBlock& x,
+__device__ __forceinline__ float small_scores(const KParams& p, const SeqCtx& s, const QBlock& x,
                                               const Tile<Cfg<KIND, D>::ELT, FAST>& tc, const SmallRegs<KIND, D>& r,
-                                              const QSrc& qsrc, RowMask& rm, int bm_head,
-                                              int pos_min, int left_max, WaveState<KIND, D, 1>& st, int lane) {
+                                              const QSrc& qsrc, RowMask& rm, int bm_head, int pos_min, int left_max,
+                                              WaveState<KIND, D, 1>& st, int lane, f32x4 (&sc)[4]) {
   using C = Cfg<KIND, D>;
-  constexpr int MD = C::MD;
   const int h = lane >> 4;
   const int J0 = tc.J0;
   float vsc;
@@ -854,7 +857,6 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
              p.bm[x.b * p.bm_sb + bm_head * p.bm_sh + qt * p.bm_sq + kt * p.bm_sk] != 0;
   }
   // S^T = K Q^T (Q operands re-read from LDS)
-  f32x4 sc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) sc[mb] = f32x4{0, 0, 0, 0};
   if constexpr (KIND == KIND_F8 && D == 128) {
@@ -882,7 +884,14 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
     mask_landmarks(sc, lmk, h);
   }
   softmax_update<KIND, D, 1>(st, 0, sc, cs);
-  // O^T += V^T P^T
+  return vsc;
+}
+
+// O^T += V^T P^T for one tile
+template <int KIND, int D>
+__device__ __forceinline__ void small_pv(const SmallRegs<KIND, D>& r, const f32x4 (&sc)[4], float vsc,
+                                         WaveState<KIND, D, 1>& st) {
+  constexpr int MD = Cfg<KIND, D>::MD;
   if constexpr (KIND == KIND_F32) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -903,6 +912,16 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
       for (int md = 0; md < MD; ++md) st.acc[0][md] = mfma_pv(v_operand<MD>(w, md), pb, st.acc[0][md]);
     }
   }
+}
+
+template <int KIND, int D, bool FAST, class QSrc>
+__device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s, const QBlock& x,
+                                              const Tile<Cfg<KIND, D>::ELT, FAST>& tc, const SmallRegs<KIND, D>& r,
+                                              const QSrc& qsrc, RowMask& rm, int bm_head,
+                                              int pos_min, int left_max, WaveState<KIND, D, 1>& st, int lane) {
+  f32x4 sc[4];
+  const float vsc = small_scores<KIND, D, FAST>(p, s, x, tc, r, qsrc, rm, bm_head, pos_min, left_max, st, lane, sc);
+  small_pv<KIND, D>(r, sc, vsc, st);
 }
 
 // One tile in flight per wave: the second wave on each SIMD (two workgroups
@@ -1046,6 +1065,15 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
 // pipeline and synchronise the workgroup at each of the many short decode
 // Q-blocks of a ragged batch.
 // ---------------------------------------------------------------------------
+#ifndef PA_HALF_STEP
+#define PA_HALF_STEP 2
+#endif
+// decode streaming with loads half a tile ahead (bit 0: bf16, bit 1: fp8).
+// fp8 only: a bf16 tile is twice the registers, and holding the next K
+// through the PV spills (measured slower); for fp8 it is ~4% faster
+template <int KIND>
+constexpr bool kHalfStep = (KIND == KIND_BF16 && (PA_HALF_STEP & 1)) || (KIND == KIND_F8 && (PA_HALF_STEP & 2));
+
 template <int KIND, int D, bool FAST>
 struct StreamRec {
   int q, t_lo;
@@ -1083,7 +1111,7 @@ struct StashLayout {   // 8 pieces (2 per wave): m[16], l[16], acc[16][D] (raw),
   }
 };
 
-template <int KIND, int D, bool FAST>
+template <int KIND, int D, bool FAST, bool WITH_V = true>
 __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c, StreamRec<KIND, D, FAST>& rec,
                                                int u, int n, int h, int lane) {
   using C = Cfg<KIND, D>;
@@ -1153,6 +1181,14 @@ __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c
     rec.t.init(p, s, tile);
   }
   small_load_k<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+  if constexpr (!WITH_V) return;
+  small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+}
+
+// The V rows of the record's tile.
+template <int KIND, int D, bool FAST>
+__device__ __forceinline__ void stream_load_v(const KParams& p, StreamRec<KIND, D, FAST>& rec, int n, int h) {
+  SeqCtx s{rec.x.b, rec.x.g, rec.x.ctx, rec.t_lo, p.bt + (int64_t)rec.x.b * p.bt_stride};
   small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
 }
 
@@ -1202,7 +1238,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
           for (int md = 0; md < MD; ++md) SL::acc(stash, k)[n * D + out_dim<KIND, D>(h, j, md)] = st.acc[0][md][j];
       }
     };
-    auto consume = [&](const StreamRec<KIND, D, FAST>& rec) {
+    auto scores = [&](const StreamRec<KIND, D, FAST>& rec, f32x4 (&sc)[4]) -> float {
       if (rec.q != cur_q) {
         if (cur_q >= 0) finish();
         cur_q = rec.q;
@@ -1217,8 +1253,8 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
         left_max = p.window > 0 ? window_left(p, cx.pos_hi) : 0;
       }
       SeqCtx s{cx.b, cx.g, cx.ctx, rec.t_lo, p.bt + (int64_t)cx.b * p.bt_stride};
-      small_compute<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromRegs<KIND, D>{rec.qB}, rm, 0, pos_min, left_max,
-                                   st, lane);
+      return small_scores<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromRegs<KIND, D>{rec.qB}, rm, 0, pos_min,
+                                         left_max, st, lane, sc);
     };
     // the Q-block of the first unit: last q with unit_prefix[q] <= wa
     int lo = 0, hi = p.hdr[H_NQB] - 1;
@@ -1231,11 +1267,29 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
     c.E = -1;                                            // forces the Q-block load on the first unit
     StreamRec<KIND, D, FAST> rec;
     rec.q = -1;
-    // one tile in flight per wave; the second wave on each SIMD (two
-    // workgroups per compute unit) computes while this one waits
-    for (int u = wa; u < wb; ++u) {
-      stream_prepare<KIND, D, FAST>(p, c, rec, u, n, h, lane);
-      consume(rec);
+    if constexpr (kHalfStep<KIND>) {
+      // half a tile ahead: the next tile's K is loaded while this tile's
+      // softmax and PV run, and its V while the next QK runs, so a wave
+      // keeps loads in flight through its compute without holding a second
+      // tile in registers
+      stream_prepare<KIND, D, FAST, false>(p, c, rec, wa, n, h, lane);
+      stream_load_v<KIND, D, FAST>(p, rec, n, h);
+      for (int u = wa; u < wb; ++u) {
+        f32x4 sc[4];
+        const float vsc = scores(rec, sc);
+        if (u + 1 < wb) stream_prepare<KIND, D, FAST, false>(p, c, rec, u + 1, n, h, lane);
+        small_pv<KIND, D>(rec.r, sc, vsc, st);
+        if (u + 1 < wb) stream_load_v<KIND, D, FAST>(p, rec, n, h);
+      }
+    } else {
+      // one tile in flight per wave; the second wave on each SIMD (two
+      // workgroups per compute unit) computes while this one waits
+      for (int u = wa; u < wb; ++u) {
+        stream_prepare<KIND, D, FAST>(p, c, rec, u, n, h, lane);
+        f32x4 sc[4];
+        const float vsc = scores(rec, sc);
+        small_pv<KIND, D>(rec.r, sc, vsc, st);
+      }
     }
     finish();
   }

@@ -91,7 +91,10 @@ def algorithmic_bytes(batch, keys_per_head):
     lse = batch.total_q * Hq * 4
     ctx = batch.seq_lens.cpu().numpy().astype(np.int64)
     bt = int(((ctx + batch.page_size - 1) // batch.page_size).sum()) * 4
-    return kv + q + o + lse + bt + batch.num_seqs * 8
+    sc = 0
+    if batch.scales is not None:                  # fp8 dequantisation scales
+        sc = sum(int(batch.scales[w].numel()) * 4 for w in ("q", "k", "v"))
+    return kv + q + o + lse + bt + sc + batch.num_seqs * 8
 
 
 def source_sha():
@@ -184,6 +187,10 @@ WORKLOADS = {
     "splitk_decode_q2_NHD": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=2, poison=False),
     "splitk_decode_q4_NHD": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=4, poison=False),
     "splitk_decode_q1_HND": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=1, kv_layout="HND", poison=False),
+    "splitk_decode_fp8_q1_NHD": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=1, kind="e4m3", poison=False),
+    "splitk_decode_fp8_q2_NHD": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=2, kind="e4m3", poison=False),
+    "splitk_decode_fp8_q4_NHD": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=4, kind="e4m3", poison=False),
+    "splitk_decode_fp8_q1_HND": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).splitk_decode(q_len=1, kind="e4m3", kv_layout="HND", poison=False),
     "hybrid_chunked": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).hybrid_chunked(poison=False),
     "prefill_bf16_dense": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="bf16", mask=False, poison=False),
     "prefill_fp8_tensor_mask": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="e4m3", quant_mode="tensor", mask=True, poison=False),
