@@ -21,10 +21,12 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = ra
 PA_F32, PA_BF16, PA_F8E4M3, PA_U8 = range(4)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_PAGE_HEAD = range(3)
 PA_SCALE_Q_PER_TOKEN_HEAD = 4
+PA_SPLIT_DYNAMIC, PA_SPLIT_STATIC = range(2)
 
 EXPORTS = ("paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_workspace_layout",
            "paged_attn_validate_host", "paged_attn_device_info", "paged_attn_status_string",
-           "paged_attn_last_hip_error", "paged_attn_kernel_timing", "paged_attn_kernel_timing_read")
+           "paged_attn_last_hip_error", "paged_attn_kernel_timing", "paged_attn_kernel_timing_read",
+           "paged_attn_plan_split")
 
 
 class pa_tensor(ctypes.Structure):
@@ -43,7 +45,8 @@ class pa_params(ctypes.Structure):
         "max_pages_per_seq", "block_table_stride", "total_q")] + [("softmax_scale", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in (
             "causal", "window", "window_expand_to_chunk", "landmark_chunk", "block_mask_tile",
-            "num_workers", "split_min_units", "force_split_units", "max_partial_slots", "flags")]
+            "num_workers", "split_min_units", "force_split_units", "max_partial_slots", "flags",
+            "split_mode", "static_splits")]
 
 
 class pa_workspace_layout(ctypes.Structure):
@@ -80,6 +83,8 @@ def lib() -> ctypes.CDLL:
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_int32]
         L.paged_attn_device_info.argtypes = [ctypes.c_int32, P(pa_device_info)]
+        L.paged_attn_plan_split.argtypes = [P(pa_params), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            P(ctypes.c_int32), P(ctypes.c_int32)]
         L.paged_attn_status_string.argtypes = [ctypes.c_int32]
         L.paged_attn_status_string.restype = ctypes.c_char_p
         L.paged_attn_last_hip_error.restype = ctypes.c_int32
@@ -138,7 +143,8 @@ def kv_logical(cache: torch.Tensor, kv_layout: str) -> pa_tensor:
 def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                 max_pages_per_seq, total_q, softmax_scale, block_table_stride=None, causal=True,
                 window=0, window_expand_to_chunk=True, landmark_chunk=0, block_mask_tile=128,
-                num_workers=0, split_min_units=0, force_split_units=0, max_partial_slots=0) -> pa_params:
+                num_workers=0, split_min_units=0, force_split_units=0, max_partial_slots=0,
+                split_mode=PA_SPLIT_DYNAMIC, static_splits=0) -> pa_params:
     p = pa_params()
     p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
     p.page_size, p.num_pages, p.max_pages_per_seq = page_size, num_pages, max_pages_per_seq
@@ -149,6 +155,7 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
     p.landmark_chunk, p.block_mask_tile = landmark_chunk, block_mask_tile
     p.num_workers, p.split_min_units, p.force_split_units = num_workers, split_min_units, force_split_units
     p.max_partial_slots, p.flags = max_partial_slots, 0
+    p.split_mode, p.static_splits = split_mode, static_splits
     return p
 
 
@@ -178,6 +185,17 @@ def paged_attn_validate_host(params: pa_params, seq_lens: torch.Tensor, query_st
     return lib().paged_attn_validate_host(ctypes.byref(params), seq_lens.data_ptr(),
                                           query_start_loc.data_ptr(), block_table.data_ptr(), mptr,
                                           mh, mq, mk)
+
+
+def paged_attn_plan_split(params: pa_params, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                          has_block_mask: bool = False):
+    """(split_mode, static_splits) the library's split policy picks for host metadata."""
+    sl = seq_lens.detach().to("cpu", torch.int32).contiguous()
+    qs = query_start_loc.detach().to("cpu", torch.int32).contiguous()
+    mode, S = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().paged_attn_plan_split(ctypes.byref(params), sl.data_ptr(), qs.data_ptr(), int(has_block_mask),
+                                       ctypes.byref(mode), ctypes.byref(S)), "paged_attn_plan_split")
+    return mode.value, S.value
 
 
 def paged_attn_device_info(device: int = 0) -> dict:
@@ -215,8 +233,8 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    softmax_scale: Optional[float] = None, kv_layout: str = "NHD", causal: bool = True,
                    window: int = 0, window_expand_to_chunk: bool = True, landmark_chunk: int = 0,
                    block_mask_tile: int = 128, num_workers: int = 0, split_min_units: int = 0,
-                   force_split_units: int = 0, max_partial_slots: int = 0,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
+                   force_split_units: int = 0, max_partial_slots: int = 0, split: str = "dynamic",
+                   static_splits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
     """Run the library on torch tensors; returns (out, lse, workspace).
 
     q [total_q, Hq, d]; k_cache/v_cache NHD [pages, page_size, Hkv, d] or HND
@@ -225,7 +243,9 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     n_k_tiles]; scales {"mode": "tensor"|"page_head", "q","k","v": fp32 device
     tensors}.  out [total_q, Hq, d] (f32 for f32 inputs, else bf16) and lse f32
     [total_q, Hq] may be strided views; missing buffers are allocated here with
-    torch (the library itself allocates nothing).
+    torch (the library itself allocates nothing).  split: "dynamic" (Assign's
+    task map), "static" (static_splits per Q-block) or "auto" (the library's
+    policy on host copies of seq_lens / query_start_loc).
     """
     total_q, Hq, d = q.shape
     if kv_layout == "NHD":
@@ -244,6 +264,13 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                          block_mask_tile=block_mask_tile, num_workers=num_workers,
                          split_min_units=split_min_units, force_split_units=force_split_units,
                          max_partial_slots=max_partial_slots)
+    if split == "auto":
+        params.split_mode, params.static_splits = paged_attn_plan_split(params, seq_lens, query_start_loc,
+                                                                        block_mask is not None)
+    elif split == "static":
+        params.split_mode, params.static_splits = PA_SPLIT_STATIC, static_splits
+    elif split != "dynamic":
+        raise ValueError("split must be 'dynamic', 'static' or 'auto'")
     out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((total_q, Hq, d), dtype=out_dtype, device=q.device)

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <cmath>
 
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -15,6 +16,7 @@ namespace pa {
 hipError_t launch_assign(const KParams& p, hipStream_t stream);
 hipError_t launch_attention(const KParams& p, int kind, int grid, hipStream_t stream);
 hipError_t launch_combine(const KParams& p, bool out_f32, int grid, hipStream_t stream);
+hipError_t launch_static_begin(const KParams& p, hipStream_t stream);
 }  // namespace pa
 
 namespace {
@@ -73,6 +75,8 @@ pa_status check_params(const pa_params* p) {
   if (p->num_workers < 0 || p->split_min_units < 0 || p->force_split_units < 0 || p->max_partial_slots < 0)
     return PA_ERR_INVALID_ARG;
   if (p->flags != 0) return PA_ERR_INVALID_ARG;
+  if (p->split_mode != PA_SPLIT_DYNAMIC && p->split_mode != PA_SPLIT_STATIC) return PA_ERR_INVALID_ARG;
+  if (p->static_splits < 0 || (p->split_mode == PA_SPLIT_STATIC && p->static_splits < 1)) return PA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
   return PA_OK;
 }
@@ -168,6 +172,55 @@ pa_status paged_attn_device_info(int32_t device, pa_device_info* info) {
   info->lds_bytes_per_workgroup = static_cast<int32_t>(prop.sharedMemPerBlock);
   info->default_workers = 2 * prop.multiProcessorCount;
   std::strncpy(info->arch, prop.gcnArchName, sizeof(info->arch) - 1);
+  return PA_OK;
+}
+
+pa_status paged_attn_plan_split(const pa_params* p, const int32_t* seq_lens_h, const int32_t* qsl_h,
+                                int32_t has_block_mask, int32_t* split_mode, int32_t* static_splits) {
+  if (!split_mode || !static_splits || !seq_lens_h || !qsl_h) return PA_ERR_INVALID_ARG;
+  pa_workspace_layout L;
+  pa_status st = layout_of(p, &L);
+  if (st != PA_OK) return st;
+  *split_mode = PA_SPLIT_DYNAMIC;
+  *static_splits = 0;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int64_t Pw = L.num_workers;
+  const int64_t L_min = p->split_min_units ? p->split_min_units : 8;
+  int64_t U = 0, T_max = 0, n_qb = int64_t(p->num_seqs) * p->num_kv_heads;
+  for (int b = 0; b < p->num_seqs; ++b) {
+    const int ql = qsl_h[b + 1] - qsl_h[b], ctx = seq_lens_h[b];
+    if (ql < 0 || ql > ctx) return PA_ERR_INVALID_ARG;
+    if (ql == 0) continue;
+    if (int64_t(ql) * G > pa::kSmallMaxRows) return PA_OK;      // static holds small Q-blocks only
+    // the Q-block's tiles, as the device counts them (positions ctx - ql .. ctx - 1)
+    const int hi = ctx - 1;
+    int lo = 0;
+    if (p->window > 0) {
+      lo = std::max(0, ctx - ql - p->window + 1);
+      if (p->window_expand_to_chunk && p->landmark_chunk > 0) lo = (lo / p->landmark_chunk) * p->landmark_chunk;
+    }
+    const int64_t n = hi >= lo ? hi / pa::kUnitKeys - lo / pa::kUnitKeys + 1 : 0;
+    U += n * p->num_kv_heads;
+    T_max = std::max(T_max, n);
+  }
+  if (has_block_mask || U == 0) return PA_OK;
+  // the busiest worker's tiles under the dynamic task map, plus Assign and Combine
+  const int64_t dyn = std::max(L_min, (U + Pw - 1) / Pw) + PA_POLICY_ASSIGN_UNITS + PA_POLICY_COMBINE_UNITS;
+  int64_t best = -1, best_S = 0;
+  const int64_t S_cap = std::max<int64_t>(1, (T_max + L_min - 1) / L_min);
+  for (int64_t S = 1; S <= S_cap; ++S) {
+    if (S > 1 && n_qb * S > L.max_slots) break;
+    const int64_t rounds = (n_qb * S + Pw - 1) / Pw;
+    const int64_t cost = rounds * ((T_max + S - 1) / S) + (S > 1 ? PA_POLICY_COMBINE_UNITS : 0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_S = S;
+    }
+  }
+  if (best >= 0 && best <= dyn) {
+    *split_mode = PA_SPLIT_STATIC;
+    *static_splits = static_cast<int32_t>(best_S);
+  }
   return PA_OK;
 }
 
@@ -270,6 +323,13 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
     if (kv_mode == PA_SCALE_PER_PAGE_HEAD && P.page_size < 64) return PA_ERR_UNSUPPORTED;
     scale_mode = scales->mode;
   }
+  const bool is_static = P.split_mode == PA_SPLIT_STATIC;
+  const int64_t n_static_qb = int64_t(P.num_seqs) * P.num_kv_heads;
+  if (is_static) {
+    if (block_mask) return PA_ERR_UNSUPPORTED;
+    if (P.static_splits > 1 && n_static_qb * P.static_splits > L.max_slots) return PA_ERR_INVALID_ARG;
+    if (n_static_qb * P.static_splits > (1 << 30)) return PA_ERR_INVALID_ARG;
+  }
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;
   if (workspace_bytes < L.total) return PA_ERR_WORKSPACE;
   if (P.total_q == 0) return PA_OK;
@@ -310,6 +370,7 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   kp.force_L = P.force_split_units;
   kp.max_slots = L.max_slots;
   kp.n_qb_max = L.n_qb_max;
+  kp.static_S = is_static ? P.static_splits : 0;
   char* ws = static_cast<char*>(workspace);
   kp.hdr = reinterpret_cast<int32_t*>(ws + L.header);
   kp.seq_qb_base = reinterpret_cast<int32_t*>(ws + L.seq_qb_base);
@@ -338,14 +399,19 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   }
   hipError_t e = hipSuccess;
   if (timing) (void)hipEventRecord(tc.ev[0], stream);
-  e = pa::launch_assign(kp, stream);
+  e = is_static ? pa::launch_static_begin(kp, stream) : pa::launch_assign(kp, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (timing) (void)hipEventRecord(tc.ev[1], stream);
-  e = pa::launch_attention(kp, kind, L.num_workers, stream);
+  const int64_t n_items = n_static_qb * P.static_splits;
+  const int grid = is_static ? static_cast<int>(std::min<int64_t>(n_items, L.num_workers)) : L.num_workers;
+  e = pa::launch_attention(kp, kind, grid, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (timing) (void)hipEventRecord(tc.ev[2], stream);
-  e = pa::launch_combine(kp, kind == pa::KIND_F32, L.num_workers, stream);
-  if (e != hipSuccess) return hip_fail(e);
+  if (!is_static || P.static_splits > 1) {
+    const int cgrid = is_static ? static_cast<int>(std::min<int64_t>(n_static_qb, L.num_workers)) : L.num_workers;
+    e = pa::launch_combine(kp, kind == pa::KIND_F32, cgrid, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (timing) {
     (void)hipEventRecord(tc.ev[3], stream);
     std::lock_guard<std::mutex> lk(g_timing_mu);

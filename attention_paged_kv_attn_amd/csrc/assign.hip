@@ -276,6 +276,28 @@ __global__ __launch_bounds__(kAssignThreads) void assign_end_kernel(KParams p) {
   assign_splits(p, p.seq_qb_base[p.B], sh, nullptr);
 }
 
+// Static split: no task map, only the header (error word cleared, sizes for
+// inspection) written before the attention kernel.
+__global__ __launch_bounds__(64) void static_begin_kernel(KParams p) {
+  if (threadIdx.x == 0) {
+    const int n_qb = p.B * p.Hkv;
+    p.hdr[H_U] = 0;
+    p.hdr[H_P] = p.P;
+    p.hdr[H_L] = 0;
+    p.hdr[H_NQB] = n_qb;
+    p.hdr[H_NSLOTS] = p.static_S > 1 ? n_qb * p.static_S : 0;
+    p.hdr[H_NCOMBINE] = p.static_S > 1 ? n_qb : 0;
+    p.hdr[H_NWORKERS] = n_qb * p.static_S;
+    p.hdr[H_ERROR] = E_NONE;
+    p.hdr[H_MAXSLOTS] = p.max_slots;
+  }
+}
+
+hipError_t launch_static_begin(const KParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(static_begin_kernel, dim3(1), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_assign(const KParams& p, hipStream_t stream) {
   if (p.bm == nullptr) {
     hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), 0, stream, p);

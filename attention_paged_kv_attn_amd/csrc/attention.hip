@@ -1913,6 +1913,39 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
 }
 
 // ---------------------------------------------------------------------------
+// static split: item it = (Q-block it / S, split it % S), mapped from the
+// workgroup id with no task map ("Triton-TLE rewrite of Tencent HPC-Ops
+// Attention", §1.2, the static Split-K variant: a fixed number of splits)
+// ---------------------------------------------------------------------------
+template <int KIND, int D, bool FAST>
+__device__ __forceinline__ void static_items(uint64_t pk) {
+  const KParams& p = kparams_at(pk);
+  const int S = p.static_S;
+  const int n_items = p.B * p.Hkv * S;
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int q = it / S, s = it - q * S;
+    QBlock x;
+    const int err = static_qblock(p, q, x);
+    if (err != E_NONE) {
+      if (threadIdx.x == 0) p.hdr[H_ERROR] = err;
+      continue;
+    }
+    if (x.ql == 0) continue;
+    const StaticSplit sp = static_split(p, x);
+    const int u0 = s * sp.c;
+    if (sp.n == 0) {
+      // no visible key: split 0 writes the empty rows
+      if (s == 0) small_segment<KIND, D, FAST>(pk, x, 0, 0, 0, 0, true, 0);
+      continue;
+    }
+    if (u0 >= sp.n) continue;
+    const bool final_out = sp.ns == 1;
+    small_segment<KIND, D, FAST>(pk, x, sp.t_lo, sp.t_lo + sp.n - 1, u0, min(sp.n, u0 + sp.c), final_out,
+                                 final_out ? 0 : it);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // the persistent kernel
 // ---------------------------------------------------------------------------
 
@@ -1921,6 +1954,10 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t pk = kparams_addr();
   const KParams& p = kparams_at(pk);
+  if (p.static_S > 0) {
+    static_items<KIND, D, FAST>(pk);
+    return;
+  }
   const int U = p.hdr[H_U];
   const int L = p.hdr[H_L];
   const int n_workers = p.hdr[H_NWORKERS];

@@ -65,13 +65,25 @@ __global__ __launch_bounds__(256) void combine_kernel(KParams p) {
   constexpr float kLn2 = 0.6931471805599453f;
   const float ninf = -__builtin_huge_valf();
   __shared__ MergeState red[256];
-  const int n_combine = p.hdr[H_NCOMBINE];
+  const bool stat = p.static_S > 0;
+  // static split: every Q-block is a candidate, its split count recomputed
+  const int n_combine = stat ? p.B * p.Hkv : p.hdr[H_NCOMBINE];
   constexpr int TPR = D / 8;
   for (int i = blockIdx.x; i < n_combine; i += gridDim.x) {
-    const int q = p.combine_list[i];
-    const QBlock x = load_qblock(p, q);
-    const int ns = p.n_splits[q];
-    const int sb = p.slot_base[q];
+    int q, ns, sb;
+    QBlock x;
+    if (stat) {
+      q = i;
+      if (static_qblock(p, q, x) != E_NONE) continue;
+      ns = static_split(p, x).ns;
+      if (ns < 2) continue;                          // written by the attention kernel
+      sb = q * p.static_S;
+    } else {
+      q = p.combine_list[i];
+      x = load_qblock(p, q);
+      ns = p.n_splits[q];
+      sb = p.slot_base[q];
+    }
     const int per = x.rows * TPR;                      // threads one pass over the rows needs
     const int groups = per >= 256 ? 1 : 256 / per;
     for (int base = 0; base < per; base += 256) {

@@ -28,7 +28,7 @@ enum HeaderField {
   H_ERROR = 7, H_MAXSLOTS = 8
 };
 
-enum DevError { E_NONE = 0, E_QSL = 1, E_QLEN = 2, E_SLOTS = 3, E_PAGE = 5 };
+enum DevError { E_NONE = 0, E_QSL = 1, E_QLEN = 2, E_SLOTS = 3, E_PAGE = 5, E_STATIC_ROWS = 6 };
 
 enum Kind { KIND_F32 = 0, KIND_BF16 = 1, KIND_F8 = 2 };
 
@@ -53,6 +53,7 @@ struct KParams {
   int32_t causal, window, expand, landmark;
   // split
   int32_t P, L_min, force_L, max_slots, n_qb_max;
+  int32_t static_S;  // > 0: static split, every Q-block cut into static_S equal tile ranges (no task map)
   // workspace
   int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
   int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;
@@ -121,6 +122,46 @@ __device__ __forceinline__ QBlock load_qblock(const KParams& p, int q) {
   x.pos_lo = x.ctx - x.ql + x.t0;
   x.pos_hi = x.pos_lo + x.nt - 1;
   return x;
+}
+
+// Static split (no task map): Q-block q is (b = q / Hkv, g = q % Hkv) and
+// holds every query token of (b, g), so each sequence needs q_len * G <= 16.
+// Reads the sequence's metadata directly; returns E_NONE or the error found.
+__device__ __forceinline__ int static_qblock(const KParams& p, int q, QBlock& x) {
+  const int b = q / p.Hkv;
+  const int q0 = p.qsl[b], q1 = p.qsl[b + 1];
+  x.b = b;
+  x.g = q - b * p.Hkv;
+  x.t0 = 0;
+  x.q0 = q0;
+  x.ql = q1 - q0;
+  x.nt = x.ql;
+  x.rows = x.ql * p.G;
+  x.ctx = p.seq_lens[b];
+  x.pos_lo = x.ctx - x.ql;
+  x.pos_hi = x.ctx - 1;
+  if (q0 < 0 || x.ql < 0 || q1 > p.total_q) return E_QSL;
+  if (x.ql > x.ctx) return E_QLEN;
+  if (x.rows > kSmallMaxRows) return E_STATIC_ROWS;
+  return E_NONE;
+}
+
+// The tiles t_lo .. t_lo + n - 1 of a static Q-block, cut into runs of
+// c = ceil(n / S) tiles; split s owns [s c, min(n, (s + 1) c)) and the ns
+// non-empty splits are 0 .. ns - 1.
+struct StaticSplit {
+  int t_lo, n, c, ns;
+};
+
+__device__ __forceinline__ StaticSplit static_split(const KParams& p, const QBlock& x) {
+  StaticSplit sp{0, 0, 1, 0};
+  int t_hi = 0;
+  if (x.ql > 0 && qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, sp.t_lo, t_hi)) {
+    sp.n = t_hi - sp.t_lo + 1;
+    sp.c = (sp.n + p.static_S - 1) / p.static_S;
+    sp.ns = (sp.n + sp.c - 1) / sp.c;
+  }
+  return sp;
 }
 
 }  // namespace pa

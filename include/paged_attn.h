@@ -122,7 +122,30 @@ typedef struct pa_params {
   int32_t force_split_units;    /* > 0: every worker gets exactly this many units (testing) */
   int32_t max_partial_slots;    /* capacity for split partial outputs; 0 = 2 * P */
   int32_t flags;                /* reserved, must be 0 */
+  int32_t split_mode;           /* pa_split_mode */
+  int32_t static_splits;        /* PA_SPLIT_STATIC: S >= 1 splits per Q-block */
 } pa_params;
+
+/* How the keys of each Q-block are cut into splits.
+ *  PA_SPLIT_DYNAMIC  Assign builds a balanced task map on the device from the
+ *                    real sequence lengths ("Triton-TLE rewrite of Tencent
+ *                    HPC-Ops Attention", §1.2 and §3.3, dynamic Split-K).
+ *  PA_SPLIT_STATIC   no task map: every Q-block (b, g) is cut into
+ *                    static_splits runs of ceil(tiles / S) 64-key tiles and
+ *                    workgroup i takes split i % S of Q-block i / S (the same
+ *                    page's static Split-K: a fixed split count, no
+ *                    rebalancing).  S = 1 is the no-split kernel: one
+ *                    workgroup per Q-block writes the output, no Combine.
+ *                    Requires q_len * Hq / Hkv <= 16 for every sequence
+ *                    (device error PA_DEV_STATIC_ROWS otherwise, those rows
+ *                    unwritten), no block mask, and, for S > 1,
+ *                    B * Hkv * S <= max_partial_slots.  Two launches (one
+ *                    when S = 1) after a one-thread header reset, instead of
+ *                    Assign's. */
+typedef enum pa_split_mode {
+  PA_SPLIT_DYNAMIC = 0,
+  PA_SPLIT_STATIC = 1
+} pa_split_mode;
 
 /* Where the Assign task map sits inside a workspace (byte offsets), for tests
  * that copy the workspace to the host and check the map bit for bit. */
@@ -155,13 +178,16 @@ typedef enum pa_device_error {
   PA_DEV_BAD_QSL = 1,        /* query_start_loc not a non-decreasing prefix ending at total_q */
   PA_DEV_BAD_QLEN = 2,       /* some q_len > seq_len */
   PA_DEV_SLOTS = 3,          /* more split partials than max_partial_slots */
-  PA_DEV_BAD_PAGE = 5        /* a block_table entry needed for a key is outside [0, num_pages) */
+  PA_DEV_BAD_PAGE = 5,       /* a block_table entry needed for a key is outside [0, num_pages) */
+  PA_DEV_STATIC_ROWS = 6     /* PA_SPLIT_STATIC with a sequence of q_len * Hq / Hkv > 16 */
 } pa_device_error;
 
 /*
  * paged_attn_fwd — the whole forward pass, enqueued on `stream` as three
  * launches: Assign (one workgroup builds the task map in the workspace),
- * the persistent split-K attention kernel (P workgroups), Combine.
+ * the persistent split-K attention kernel (P workgroups), Combine; with
+ * PA_SPLIT_STATIC, a one-thread header reset, the attention kernel and
+ * (S > 1) Combine.
  *
  *  q            [total_q, Hq, d], dtype f32 | bf16 | e4m3; strides for the
  *               first two dims are free (d contiguous).
@@ -206,6 +232,24 @@ pa_status paged_attn_workspace_size(const pa_params* params, size_t* bytes);
 
 /* Offsets of the task map inside the workspace (host only). */
 pa_status paged_attn_workspace_layout(const pa_params* params, pa_workspace_layout* layout);
+
+/* The split policy: picks PA_SPLIT_STATIC (and its S) or PA_SPLIT_DYNAMIC
+ * for a batch from its metadata in host memory, the host-side choice of a
+ * kernel variant by sequence shape that "Triton-TLE rewrite of Tencent HPC-Ops
+ * Attention", §1.2 and §3 describe, with the grid-saturation test of
+ * "HiLS-Attention", split-KV decode.  Static is chosen only when every
+ * sequence fits one small Q-block, there is no block mask, and the static
+ * cut's busiest workgroup carries no more 64-key tiles than the dynamic
+ * task map's would plus the cost of its Assign launch (counted as
+ * PA_POLICY_ASSIGN_UNITS tiles) and of a Combine (PA_POLICY_COMBINE_UNITS);
+ * among static cuts the one with the fewest tiles on its busiest workgroup
+ * wins.  Writes split_mode and static_splits; reads nothing on the device
+ * except, when params->num_workers is 0, the compute-unit count. */
+#define PA_POLICY_ASSIGN_UNITS 3
+#define PA_POLICY_COMBINE_UNITS 2
+pa_status paged_attn_plan_split(const pa_params* params, const int32_t* seq_lens_h,
+                                const int32_t* query_start_loc_h, int32_t has_block_mask,
+                                int32_t* split_mode, int32_t* static_splits);
 
 /* Host-side check of batch metadata held in host memory: query_start_loc is a
  * prefix ending at total_q, 0 <= q_len <= seq_len, every block_table entry a

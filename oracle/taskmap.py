@@ -47,6 +47,16 @@ Specification
   Q-blocks with n_splits != 1 go, in order, into the combine list.
   Q-blocks with n_splits >= 2 get partial slots slot_base(q) = running sum of
   n_splits over earlier such Q-blocks (-1 for the others); n_slots = total.
+
+Static split (no task map)
+--------------------------
+* The static variant of the same page's Split-K (a fixed number of splits
+  per request, no Assign): every sequence must fit one small Q-block
+  (q_len * G <= 16), Q-block q = (b = q // Hkv, g = q % Hkv).  Its tiles
+  tile_lo .. tile_lo + n - 1 (the range above; no block mask) are cut into
+  runs of c = ceil(n / S); split s owns [s c, min(n, (s + 1) c)); the
+  ns = ceil(n / c) non-empty splits come first.  Item i = q S + s is split
+  s of Q-block q, and writes partial slot i when ns >= 2.
 """
 import numpy as np
 
@@ -149,3 +159,30 @@ def build(seq_lens, query_start_loc, *, Hq, Hkv, num_workers, split_min_units=8,
         "U": U, "P": P, "L": L, "n_qb": len(descs), "n_slots": slots,
         "n_workers": -(-U // L) if U else 0,
     }
+
+
+def static_map(seq_lens, query_start_loc, *, Hq, Hkv, S, causal=True, window=0,
+               window_expand_to_chunk=True, landmark_chunk=0):
+    """Per item (q, s): (b, g, first tile, tile count) of the static split; raises
+    when a sequence does not fit one small Q-block."""
+    G = Hq // Hkv
+    seq_lens = [int(x) for x in seq_lens]
+    qsl = [int(x) for x in query_start_loc]
+    items = []
+    for b in range(len(seq_lens)):
+        ql, ctx = qsl[b + 1] - qsl[b], seq_lens[b]
+        if ql * G > SMALL_MAX_ROWS:
+            raise ValueError(f"sequence {b}: q_len {ql} does not fit one small Q-block")
+        for g in range(Hkv):
+            n, t_lo = 0, 0
+            if ql > 0:
+                pos_lo, pos_hi = ctx - ql, ctx - 1
+                hi = min(ctx - 1, pos_hi) if causal else ctx - 1
+                lo = _window_left(pos_lo, window, window_expand_to_chunk, landmark_chunk) if window > 0 else 0
+                if hi >= lo:
+                    t_lo, n = lo // UNIT_KEYS, hi // UNIT_KEYS - lo // UNIT_KEYS + 1
+            c = -(-n // S) if n else 1
+            for s in range(S):
+                a = min(n, s * c)
+                items.append((b, g, t_lo + a, min(n, a + c) - a if s * c < n else 0))
+    return items

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -162,3 +163,50 @@ def test_validate_host():
     p2 = B.make_params(num_seqs=3, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16, num_pages=64,
                        max_pages_per_seq=13, total_q=18, softmax_scale=0.125, num_workers=4)
     assert B.paged_attn_validate_host(p2, long_ctx, qsl, bt2, mask) == B.PA_ERR_INVALID_ARG
+
+
+def _plan(ctx, ql, *, Hq=32, Hkv=8, P=512, mask=False, **kw):
+    import torch
+    qsl = [0]
+    for x in ql:
+        qsl.append(qsl[-1] + x)
+    params = B.make_params(num_seqs=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=64,
+                           num_pages=1 << 20, max_pages_per_seq=max(1, -(-max(ctx) // 64)),
+                           total_q=qsl[-1], softmax_scale=0.088, num_workers=P, **kw)
+    return B.paged_attn_plan_split(params, torch.tensor(ctx, dtype=torch.int32),
+                                   torch.tensor(qsl, dtype=torch.int32), mask)
+
+
+def test_split_policy_choices():
+    """The policy's documented rule on shapes worked out by hand:
+    busiest worker under the dynamic map = max(8, ceil(U / P)) + 3 + 2 tiles,
+    under a static cut = ceil(n_qb S / P) * ceil(T_max / S) (+ 2 when S > 1)."""
+    rng = np.random.default_rng(2)
+    loguni = np.clip(np.rint(np.exp(rng.uniform(np.log(128), np.log(32768), 64))), 128, 32768).astype(int)
+    # ragged decode: a static cut leaves the longest sequence on one workgroup -> dynamic
+    assert _plan(loguni.tolist(), [1] * 64) == (B.PA_SPLIT_DYNAMIC, 0)
+    # uniform decode, 512 Q-blocks of 64 tiles on 512 workers: no split (64 <= 64 + 5)
+    assert _plan([4096] * 64, [1] * 64) == (B.PA_SPLIT_STATIC, 1)
+    # one 128K sequence, 8 Q-blocks of 2048 tiles: S = 64 gives 32 + 2 <= 32 + 5
+    assert _plan([131072], [1], P=512) == (B.PA_SPLIT_STATIC, 64)
+    # windowed 128K decode: the window starts on a 64-key boundary, so 64 tiles
+    # per Q-block; at most ceil(64 / 8) = 8 splits of 8 tiles -> 8 + 2 = 10 <= max(8, 1) + 5
+    assert _plan([131072], [1], window=4096, landmark_chunk=64) == (B.PA_SPLIT_STATIC, 8)
+    # prefill rows (q_len * G > 16) and block masks are dynamic only
+    assert _plan([4096] * 4, [512] * 4) == (B.PA_SPLIT_DYNAMIC, 0)
+    assert _plan([4096] * 64, [1] * 64, mask=True) == (B.PA_SPLIT_DYNAMIC, 0)
+    # MTP 4 with G = 4 is still one small Q-block per (b, g)
+    assert _plan([4096] * 64, [4] * 64) == (B.PA_SPLIT_STATIC, 1)
+
+
+def test_static_split_argument_checks():
+    import torch
+    params = B.make_params(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16, num_pages=8,
+                           max_pages_per_seq=4, total_q=2, softmax_scale=0.125, num_workers=4,
+                           split_mode=B.PA_SPLIT_STATIC, static_splits=0)
+    n = ctypes.c_size_t()
+    assert B.lib().paged_attn_workspace_size(ctypes.byref(params), ctypes.byref(n)) == B.PA_ERR_INVALID_ARG
+    params.static_splits = 2
+    assert B.lib().paged_attn_workspace_size(ctypes.byref(params), ctypes.byref(n)) == B.PA_OK
+    params.split_mode = 7
+    assert B.lib().paged_attn_workspace_size(ctypes.byref(params), ctypes.byref(n)) == B.PA_ERR_INVALID_ARG

@@ -355,6 +355,99 @@ def test_sliding_window_decode_128k():
 
 
 # ---------------------------------------------------------------------------
+# static split (no task map) and the split policy
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 3, 8])
+@pytest.mark.parametrize("kind,q_len,layout", [("bf16", 1, "NHD"), ("bf16", 4, "HND"), ("e4m3", 2, "NHD")])
+def test_static_split_decode(S, kind, q_len, layout):
+    b = W.splitk_decode(q_len=q_len, kv_layout=layout, batch=12, ctx_lo=100, ctx_hi=6000, kind=kind)
+    g, out, lse, ws = gpu_run(b, split="static", static_splits=S)
+    h = check_no_device_error(ws, g)
+    assert h[3] == 12 * 8 and h[6] == 12 * 8 * S
+    compare(b, out, lse)
+
+
+def test_static_split_partials_follow_the_static_map():
+    """Each split's partial LSE and O in its slot equal attention over exactly
+    the keys the static map gives that split."""
+    S = 4
+    b = W.splitk_decode(q_len=2, batch=5, ctx_lo=300, ctx_hi=3000)
+    g, out, lse, ws = gpu_run(b, split="static", static_splits=S)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    lay = B.paged_attn_workspace_layout(params_of(g))
+    D = b.head_dim
+    plse = ws[lay.partial_lse:lay.partial_lse + lay.max_slots * 128 * 4].view(torch.float32).cpu()
+    plse = plse.numpy().reshape(lay.max_slots, 128)
+    po = ws[lay.partial_o:lay.partial_o + lay.max_slots * 128 * D * 4].view(torch.float32).cpu()
+    po = po.numpy().reshape(lay.max_slots, 128, D)
+    ctx = b.seq_lens.numpy()
+    qsl = b.query_start_loc.numpy()
+    G = b.num_q_heads // b.num_kv_heads
+    items = taskmap.static_map(ctx, qsl, Hq=b.num_q_heads, Hkv=b.num_kv_heads, S=S)
+    checked = 0
+    for it, (bb, gg, t0, n) in enumerate(items):
+        q = it // S
+        if n == 0 or sum(1 for x in items[q * S:(q + 1) * S] if x[3]) < 2:
+            continue
+        kr = np.zeros((b.num_seqs, 2), np.int64)
+        kr[bb] = (64 * t0, min(int(ctx[bb]), 64 * (t0 + n)))
+        rows = np.zeros(b.total_q, bool)
+        rows[qsl[bb]:qsl[bb + 1]] = True
+        O, L = run_oracle(b, key_range=kr, rows=rows)
+        for r in range((qsl[bb + 1] - qsl[bb]) * G):
+            tok, head = qsl[bb] + r // G, gg * G + r % G
+            assert abs(plse[it, r] - L[tok, head]) <= 1e-3
+            assert np.abs(po[it, r] - O[tok, head]).max() <= 2e-2
+        checked += 1
+    say(f"  checked {checked} split partials")
+    assert checked > 10
+
+
+def test_static_split_windowed_and_full_128k_decode():
+    b = W.sliding_window(decode=True)
+    g, out, lse, ws = gpu_run(b, split="auto")
+    mode, S = B.paged_attn_plan_split(params_of(g), b.seq_lens, b.query_start_loc)
+    assert mode == B.PA_SPLIT_STATIC and S == 8
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    b.window, b.landmark_chunk = 0, 0
+    g, out, lse, ws = gpu_run(b, split="auto")
+    assert B.paged_attn_plan_split(params_of(g), b.seq_lens, b.query_start_loc) == (B.PA_SPLIT_STATIC, 64)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+def test_static_split_edges_and_rows_too_large():
+    rng = np.random.default_rng(23)
+    # empty sequences, a single key, a Q-block with fewer tiles than splits
+    b = W.build_batch(rng, name="static_edges", kind="bf16", Hq=8, Hkv=2, d=128, page_size=16,
+                      ctx=[1, 65, 0, 130, 7, 64, 900], q_len=[1, 3, 0, 0, 4, 2, 1], num_pages=120)
+    g, out, lse, ws = gpu_run(b, split="static", static_splits=5)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    # a sequence whose rows do not fit one small Q-block: reported, other rows still right
+    b = W.build_batch(rng, name="static_too_big", kind="bf16", Hq=8, Hkv=2, d=64, page_size=64,
+                      ctx=[300, 200, 500], q_len=[1, 5, 2], num_pages=20)
+    g, out, lse, ws = gpu_run(b, split="static", static_splits=2)
+    h, _ = header(ws, params_of(g))
+    assert h[7] == 6
+    rows = np.ones(b.total_q, bool)
+    rows[1:6] = False
+    compare(b, out, lse, rows=rows)
+
+
+def test_auto_policy_runs_each_shape():
+    for b in (W.splitk_decode(q_len=1, batch=12, ctx_lo=100, ctx_hi=6000),
+              W.build_batch(np.random.default_rng(5), name="uniform", kind="bf16", Hq=32, Hkv=8, d=128,
+                            page_size=64, ctx=[2048] * 64, q_len=[1] * 64),
+              W.hybrid_chunked(batch=8, chunk=256, history=700, dec_lo=300, dec_hi=2000)):
+        g, out, lse, ws = gpu_run(b, split="auto")
+        check_no_device_error(ws, g)
+        compare(b, out, lse)
+
+
+# ---------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------
 def test_page_permutation_bitwise():

@@ -125,3 +125,39 @@ def test_large_q_blocks_zigzag_and_cover_every_token_once():
     assert tokens == list(range(300)) and seq0[1][3] == 300 - 9 * 32
     # decode sequence: one small Q-block per kv head
     assert [d for d in qb if d[0] == 1] == [(1, 0, 0, 1), (1, 1, 0, 1)]
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("rule", [dict(causal=True), dict(causal=True, window=200, chunk=64),
+                                  dict(causal=False)])
+def test_static_map_partitions_each_q_block(S, rule):
+    """Static splits cover the Q-block's visible tiles exactly once, the
+    non-empty splits first, each of ceil(n / S) tiles but the last."""
+    ctx = [37, 300, 1, 4100, 64, 65]
+    ql = [1, 4, 1, 2, 0, 1]
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    kw = dict(causal=rule.get("causal", True), window=rule.get("window", 0),
+              window_expand_to_chunk=True, landmark_chunk=rule.get("chunk", 0))
+    items = taskmap.static_map(ctx, qsl, Hq=8, Hkv=2, S=S, **kw)
+    assert len(items) == len(ctx) * 2 * S
+    for q in range(len(ctx) * 2):
+        b, g = q // 2, q % 2
+        mine = items[q * S:(q + 1) * S]
+        assert all(it[0] == b and it[1] == g for it in mine)
+        covered = [t for (_, _, t0, n) in mine for t in range(t0, t0 + n)]
+        assert len(covered) == len(set(covered))
+        # brute force: tiles with a key some row of the Q-block may see
+        want = _brute_units((b, g, 0, ql[b]), ctx[b], ql[b], **rule) if ql[b] else 0
+        assert len(covered) == want
+        if want:
+            assert covered == list(range(min(covered), min(covered) + want))
+        sizes = [n for (_, _, _, n) in mine]
+        nz = [x for x in sizes if x]
+        assert sizes[:len(nz)] == nz                       # non-empty splits first
+        c = -(-want // S) if want else 1
+        assert all(x == c for x in nz[:-1]) and (not nz or 0 < nz[-1] <= c)
+
+
+def test_static_map_rejects_large_q_blocks():
+    with pytest.raises(ValueError):
+        taskmap.static_map([100], [0, 5], Hq=32, Hkv=8, S=2)        # 5 tokens x G 4 = 20 rows > 16
