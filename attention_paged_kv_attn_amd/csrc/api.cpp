@@ -14,7 +14,7 @@
 
 namespace pa {
 hipError_t launch_assign(const KParams& p, hipStream_t stream);
-hipError_t launch_attention(const KParams& p, int kind, int grid, hipStream_t stream);
+hipError_t launch_attention(const KParams& p, int kind, int grid, bool small_only, hipStream_t stream);
 hipError_t launch_combine(const KParams& p, bool out_f32, int grid, hipStream_t stream);
 hipError_t launch_static_begin(const KParams& p, hipStream_t stream);
 }  // namespace pa
@@ -77,6 +77,7 @@ pa_status check_params(const pa_params* p) {
   if (p->flags != 0) return PA_ERR_INVALID_ARG;
   if (p->split_mode != PA_SPLIT_DYNAMIC && p->split_mode != PA_SPLIT_STATIC) return PA_ERR_INVALID_ARG;
   if (p->static_splits < 0 || (p->split_mode == PA_SPLIT_STATIC && p->static_splits < 1)) return PA_ERR_INVALID_ARG;
+  if (p->max_q_len < 0) return PA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
   return PA_OK;
 }
@@ -371,6 +372,7 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   kp.max_slots = L.max_slots;
   kp.n_qb_max = L.n_qb_max;
   kp.static_S = is_static ? P.static_splits : 0;
+  kp.max_q_len = P.max_q_len;
   char* ws = static_cast<char*>(workspace);
   kp.hdr = reinterpret_cast<int32_t*>(ws + L.header);
   kp.seq_qb_base = reinterpret_cast<int32_t*>(ws + L.seq_qb_base);
@@ -404,7 +406,9 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   if (timing) (void)hipEventRecord(tc.ev[1], stream);
   const int64_t n_items = n_static_qb * P.static_splits;
   const int grid = is_static ? static_cast<int>(std::min<int64_t>(n_items, L.num_workers)) : L.num_workers;
-  e = pa::launch_attention(kp, kind, grid, stream);
+  // the small-Q-block kernel when every Q-block is known to be small
+  const bool small_only = is_static || (P.max_q_len > 0 && int64_t(P.max_q_len) * kp.G <= pa::kSmallMaxRows);
+  e = pa::launch_attention(kp, kind, grid, small_only, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (timing) (void)hipEventRecord(tc.ev[2], stream);
   if (!is_static || P.static_splits > 1) {

@@ -1111,6 +1111,25 @@ struct StashLayout {   // 8 pieces (2 per wave): m[16], l[16], acc[16][D] (raw),
   }
 };
 
+// The Q-block holding unit a: the last q in [lo, hi] with unit_prefix[q] <= a
+// (unit_prefix[lo] <= a).  A 64-way search: each round probes 64 evenly
+// spaced entries with one vector load, so ceil(log64(n)) dependent loads
+// instead of a binary search's log2(n), which at kernel start (every worker
+// searching at once, nothing else in flight) is pure latency.
+__device__ __forceinline__ int find_qblock(const KParams& p, int lo, int hi, int a, int lane) {
+  lo = wave_uniform(lo);
+  hi = wave_uniform(hi);
+  while (lo < hi) {
+    const int step = (hi - lo + 64) >> 6;
+    const int idx = lo + lane * step;
+    const bool ok = idx <= hi && p.unit_prefix[min(idx, hi)] <= a;
+    const uint64_t m = __ballot(ok);                    // lane 0 is always set
+    lo = wave_uniform(lo + (63 - __builtin_clzll(m)) * step);
+    hi = wave_uniform(min(hi, lo + step - 1));
+  }
+  return lo;
+}
+
 template <int KIND, int D, bool FAST, bool WITH_V = true>
 __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c, StreamRec<KIND, D, FAST>& rec,
                                                int u, int n, int h, int lane) {
@@ -1180,16 +1199,25 @@ __device__ __forceinline__ void stream_prepare(const KParams& p, StreamCursor& c
   } else {
     rec.t.init(p, s, tile);
   }
-  small_load_k<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+  // the lane's row and column come from an opaque copy of the thread id: the
+  // per-lane load offsets are then rebuilt for each tile (a few VALU ops)
+  // instead of being hoisted out of the loop, where under the kernel's
+  // register pressure they were spilled, and the reload from scratch
+  // (counted with the vector loads) made the V loads wait for the K loads
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  small_load_k<KIND, D, FAST>(p, s, rec.t, rec.r, tid & 15, (tid >> 4) & 3);
   if constexpr (!WITH_V) return;
-  small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+  small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, tid & 15, (tid >> 4) & 3);
 }
 
 // The V rows of the record's tile.
 template <int KIND, int D, bool FAST>
 __device__ __forceinline__ void stream_load_v(const KParams& p, StreamRec<KIND, D, FAST>& rec, int n, int h) {
   SeqCtx s{rec.x.b, rec.x.g, rec.x.ctx, rec.t_lo, p.bt + (int64_t)rec.x.b * p.bt_stride};
-  small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, n, h);
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  small_load_v<KIND, D, FAST>(p, s, rec.t, rec.r, tid & 15, (tid >> 4) & 3);
 }
 
 template <int KIND, int D, bool FAST>
@@ -1256,14 +1284,9 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
       return small_scores<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromRegs<KIND, D>{rec.qB}, rm, 0, pos_min,
                                          left_max, st, lane, sc);
     };
-    // the Q-block of the first unit: last q with unit_prefix[q] <= wa
-    int lo = 0, hi = p.hdr[H_NQB] - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.unit_prefix[mid] <= wa) lo = mid; else hi = mid - 1;
-    }
+    // the Q-block of the first unit
     StreamCursor c;
-    c.q = wave_uniform(lo);
+    c.q = find_qblock(p, 0, p.hdr[H_NQB] - 1, wa, lane);
     c.E = -1;                                            // forces the Q-block load on the first unit
     StreamRec<KIND, D, FAST> rec;
     rec.q = -1;
@@ -1949,14 +1972,22 @@ __device__ __forceinline__ void static_items(uint64_t pk) {
 // the persistent kernel
 // ---------------------------------------------------------------------------
 
-template <int KIND, int D, bool FAST>
+// SMALL: the kernel for batches whose Q-blocks are all small (decode and
+// MTP, and every static split).  It is the same code without the large-Q-block
+// path, compiled on its own: sharing a kernel with the large path's register
+// demand slows the decode loops (measured 7-13%), although their instruction
+// streams come out nearly the same.  A large Q-block reaching it is reported
+// (E_QLEN_HINT) and skipped.
+template <int KIND, int D, bool FAST, bool SMALL>
 __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention_kernel(KParams) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t pk = kparams_addr();
   const KParams& p = kparams_at(pk);
-  if (p.static_S > 0) {
-    static_items<KIND, D, FAST>(pk);
-    return;
+  if constexpr (SMALL) {
+    if (p.static_S > 0) {
+      static_items<KIND, D, FAST>(pk);
+      return;
+    }
   }
   const int U = p.hdr[H_U];
   const int L = p.hdr[H_L];
@@ -1974,13 +2005,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   for (int vw = rank; vw < n_workers; vw += gridDim.x) {
     int a = vw * L;
     const int b_end = min(a + L, U);
-    // Q-block containing unit a: last q with unit_prefix[q] <= a
-    int lo = 0, hi = n_qb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.unit_prefix[mid] <= a) lo = mid; else hi = mid - 1;
-    }
-    int q = lo;
+    int q = find_qblock(p, 0, n_qb - 1, a, threadIdx.x & 63);
     while (a < b_end && q < n_qb) {
       const int S = p.unit_prefix[q], nq = p.unit_prefix[q + 1] - S;
       if (nq == 0) { ++q; continue; }
@@ -2006,40 +2031,50 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
       const bool final_out = p.n_splits[q] == 1;
       const int slot = final_out ? 0 : p.slot_base[q] + (vw - S / L);
       if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
-      else large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot, ds);
+      else if constexpr (SMALL) {
+        if (threadIdx.x == 0) p.hdr[H_ERROR] = E_QLEN_HINT;
+      } else {
+        large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot, ds);
+      }
       a = S + u1;
       ++q;
     }
   }
 }
 
-template <int KIND, int D, bool FAST>
+template <int KIND, int D, bool FAST, bool SMALL>
 static hipError_t launch_attention_t(const KParams& p, int grid, hipStream_t stream) {
   const int lds = Lds<KIND, D, FAST>::DYN;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST, SMALL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL((attention_kernel<KIND, D, FAST>), dim3(grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((attention_kernel<KIND, D, FAST, SMALL>), dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-template <int KIND, int D>
+template <int KIND, int D, bool SMALL>
 static hipError_t launch_attention_kd(const KParams& p, int grid, hipStream_t stream) {
-  return p.page_size >= kUnitKeys ? launch_attention_t<KIND, D, true>(p, grid, stream)
-                                  : launch_attention_t<KIND, D, false>(p, grid, stream);
+  return p.page_size >= kUnitKeys ? launch_attention_t<KIND, D, true, SMALL>(p, grid, stream)
+                                  : launch_attention_t<KIND, D, false, SMALL>(p, grid, stream);
 }
 
-hipError_t launch_attention(const KParams& p, int kind, int grid, hipStream_t stream) {
-  if (kind == KIND_F32) return p.D == 64 ? launch_attention_kd<KIND_F32, 64>(p, grid, stream)
-                                         : launch_attention_kd<KIND_F32, 128>(p, grid, stream);
-  if (kind == KIND_BF16) return p.D == 64 ? launch_attention_kd<KIND_BF16, 64>(p, grid, stream)
-                                          : launch_attention_kd<KIND_BF16, 128>(p, grid, stream);
-  return p.D == 64 ? launch_attention_kd<KIND_F8, 64>(p, grid, stream)
-                   : launch_attention_kd<KIND_F8, 128>(p, grid, stream);
+template <bool SMALL>
+static hipError_t launch_attention_s(const KParams& p, int kind, int grid, hipStream_t stream) {
+  if (kind == KIND_F32) return p.D == 64 ? launch_attention_kd<KIND_F32, 64, SMALL>(p, grid, stream)
+                                         : launch_attention_kd<KIND_F32, 128, SMALL>(p, grid, stream);
+  if (kind == KIND_BF16) return p.D == 64 ? launch_attention_kd<KIND_BF16, 64, SMALL>(p, grid, stream)
+                                          : launch_attention_kd<KIND_BF16, 128, SMALL>(p, grid, stream);
+  return p.D == 64 ? launch_attention_kd<KIND_F8, 64, SMALL>(p, grid, stream)
+                   : launch_attention_kd<KIND_F8, 128, SMALL>(p, grid, stream);
+}
+
+hipError_t launch_attention(const KParams& p, int kind, int grid, bool small_only, hipStream_t stream) {
+  return small_only ? launch_attention_s<true>(p, kind, grid, stream)
+                    : launch_attention_s<false>(p, kind, grid, stream);
 }
 
 }  // namespace pa

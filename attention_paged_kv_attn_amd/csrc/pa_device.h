@@ -28,7 +28,7 @@ enum HeaderField {
   H_ERROR = 7, H_MAXSLOTS = 8
 };
 
-enum DevError { E_NONE = 0, E_QSL = 1, E_QLEN = 2, E_SLOTS = 3, E_PAGE = 5, E_STATIC_ROWS = 6 };
+enum DevError { E_NONE = 0, E_QSL = 1, E_QLEN = 2, E_SLOTS = 3, E_PAGE = 5, E_STATIC_ROWS = 6, E_QLEN_HINT = 7 };
 
 enum Kind { KIND_F32 = 0, KIND_BF16 = 1, KIND_F8 = 2 };
 
@@ -54,6 +54,7 @@ struct KParams {
   // split
   int32_t P, L_min, force_L, max_slots, n_qb_max;
   int32_t static_S;  // > 0: static split, every Q-block cut into static_S equal tile ranges (no task map)
+  int32_t max_q_len; // > 0: the caller's bound on every q_len (checked by Assign)
   // workspace
   int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
   int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;

@@ -63,6 +63,7 @@ class PagedBatch:
     dense_k: Optional[list] = None  # per sequence [ctx, Hkv, d] stored values (tiny workloads only)
     dense_v: Optional[list] = None
     info: dict = field(default_factory=dict)
+    max_q_len: int = 0            # the largest q_len of the batch (0 = not stated)
 
     @property
     def num_seqs(self) -> int:
@@ -255,7 +256,7 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
                       causal=causal, window=window, window_expand_to_chunk=window_expand_to_chunk,
                       landmark_chunk=landmark_chunk, block_mask=block_mask, block_mask_tile=block_mask_tile,
                       scales=scales, out_heads_major=out_heads_major, dense_k=dense_k, dense_v=dense_v,
-                      info=info)
+                      info=info, max_q_len=max(q_len) if q_len else 0)
 
 
 # ---------------------------------------------------------------------------
@@ -303,6 +304,17 @@ def splitk_decode(q_len=1, kv_layout: str = "NHD", seed: int = 2, batch: int = 6
                        poison=poison, keep_dense=keep_dense,
                        quant_mode=quant_mode if kind == "e4m3" else None,
                        q_quant=q_quant if kind == "e4m3" else "tensor")
+
+
+def uniform_decode(ctx: int = 4096, batch: int = 64, q_len: int = 1, seed: int = 6, poison: bool = True,
+                   kind: str = "bf16") -> PagedBatch:
+    """Decode batch whose sequences all hold `ctx` keys (Llama-3.1-8B heads,
+    64-token pages in a random permutation): the shape a static split suits."""
+    rng = np.random.default_rng(seed)
+    return build_batch(rng, name=f"uniform_decode_{ctx}_q{q_len}", kind=kind, Hq=32, Hkv=8, d=128,
+                       page_size=64, ctx=[ctx] * batch, q_len=[q_len] * batch, poison=poison,
+                       quant_mode="tensor" if kind == "e4m3" else None,
+                       q_quant="token_head" if kind == "e4m3" else "tensor")
 
 
 def hybrid_chunked(seed: int = 3, chunk_last: bool = False, poison: bool = True,

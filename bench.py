@@ -128,14 +128,35 @@ def traffic_for(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_workload(batch, steps, warmup):
+def split_kw(spec, g):
+    """Launch options for a split spec: dynamic, auto (the library's policy,
+    decided once on the host before timing) or static<S>."""
+    from attention_paged_kv_attn_amd import binding as B
+    if spec in (None, "dynamic"):
+        return {}
+    if spec == "auto":
+        params = B.make_params(num_seqs=g.num_seqs, num_q_heads=g.num_q_heads, num_kv_heads=g.num_kv_heads,
+                               head_dim=g.head_dim, page_size=g.page_size, num_pages=g.num_pages,
+                               max_pages_per_seq=g.block_table.shape[1], total_q=g.total_q,
+                               softmax_scale=g.softmax_scale, causal=g.causal, window=g.window,
+                               window_expand_to_chunk=g.window_expand_to_chunk, landmark_chunk=g.landmark_chunk)
+        mode, S = B.paged_attn_plan_split(params, g.seq_lens, g.query_start_loc, g.block_mask is not None)
+        log(f"split policy: {'static S=%d' % S if mode == B.PA_SPLIT_STATIC else 'dynamic'}")
+        return {"split": "static", "static_splits": S} if mode == B.PA_SPLIT_STATIC else {}
+    if spec.startswith("static"):
+        return {"split": "static", "static_splits": int(spec[len("static"):])}
+    raise ValueError(spec)
+
+
+def time_workload(batch, steps, warmup, split=None):
     import torch
     from attention_paged_kv_attn_amd import binding as B
     g = batch.to("cuda:0")
-    out, lse, ws = B.run_batch(g)            # allocates outputs + workspace once
+    kw = split_kw(split, g)
+    out, lse, ws = B.run_batch(g, **kw)      # allocates outputs + workspace once
     torch.cuda.synchronize()
     for _ in range(warmup):
-        B.run_batch(g, out=out, lse=lse, workspace=ws)
+        B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
     torch.cuda.synchronize()
     B.paged_attn_kernel_timing_read()         # clear
     B.paged_attn_kernel_timing(True)
@@ -144,7 +165,7 @@ def time_workload(batch, steps, warmup):
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(steps):
-        B.run_batch(g, out=out, lse=lse, workspace=ws)
+        B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
     t1.record(stream)
     torch.cuda.synchronize()
     B.paged_attn_kernel_timing(False)
@@ -197,6 +218,8 @@ WORKLOADS = {
     "prefill_fp8_tensor_dense": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="e4m3", quant_mode="tensor", mask=False, poison=False),
     "window_fwd": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sliding_window(poison=False),
     "window_decode_128k_full": lambda: _full_decode_128k(),
+    "window_decode_128k": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sliding_window(decode=True, poison=False),
+    "uniform_decode_4k": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).uniform_decode(poison=False),
 }
 
 
@@ -207,14 +230,16 @@ def _full_decode_128k():
 
 
 def leg(name, steps, warmup):
+    """name is a workload, optionally '@dynamic', '@auto' or '@static<S>'."""
+    name, _, split = name.partition("@")
     log(f"generating {name}")
     batch = WORKLOADS[name]()
     pairs, keys = visible_pairs_and_keys(batch)
     by = algorithmic_bytes(batch, keys)
     flops = 4.0 * batch.head_dim * pairs
     log(f"{name}: {by / 1e9:.3f} GB algorithmic, {flops / 1e12:.4f} TFLOP; timing {steps} steps")
-    ms, kms, _ = time_workload(batch, steps, warmup)
-    log(f"{name}: {ms:.4f} ms/step; kernels {kms}")
+    ms, kms, _ = time_workload(batch, steps, warmup, split or None)
+    log(f"{name}@{split or 'dynamic'}: {ms:.4f} ms/step; kernels {kms}")
     return batch, by, flops, ms, kms
 
 

@@ -124,6 +124,12 @@ typedef struct pa_params {
   int32_t flags;                /* reserved, must be 0 */
   int32_t split_mode;           /* pa_split_mode */
   int32_t static_splits;        /* PA_SPLIT_STATIC: S >= 1 splits per Q-block */
+  int32_t max_q_len;            /* 0, or a bound on every sequence's q_len known to the caller
+                                   (a scheduler's max query length).  When max_q_len * Hq / Hkv
+                                   <= 16 every Q-block is small and a kernel built without the
+                                   prefill path runs (faster decode).  A sequence longer than
+                                   the bound is device error PA_DEV_QLEN_HINT (outputs then
+                                   unspecified). */
 } pa_params;
 
 /* How the keys of each Q-block are cut into splits.
@@ -179,7 +185,8 @@ typedef enum pa_device_error {
   PA_DEV_BAD_QLEN = 2,       /* some q_len > seq_len */
   PA_DEV_SLOTS = 3,          /* more split partials than max_partial_slots */
   PA_DEV_BAD_PAGE = 5,       /* a block_table entry needed for a key is outside [0, num_pages) */
-  PA_DEV_STATIC_ROWS = 6     /* PA_SPLIT_STATIC with a sequence of q_len * Hq / Hkv > 16 */
+  PA_DEV_STATIC_ROWS = 6,    /* PA_SPLIT_STATIC with a sequence of q_len * Hq / Hkv > 16 */
+  PA_DEV_QLEN_HINT = 7       /* a sequence's q_len exceeds params->max_q_len */
 } pa_device_error;
 
 /*

@@ -437,6 +437,31 @@ def test_static_split_edges_and_rows_too_large():
     compare(b, out, lse, rows=rows)
 
 
+def test_decode_kernel_choice_by_q_len_bound():
+    """Decode batches run the small-Q-block kernel when the caller states
+    max_q_len (run_batch passes the batch's own); the general kernel, chosen
+    without the bound, gives the same result; a bound below a sequence's
+    q_len is reported."""
+    b = W.splitk_decode(q_len=[1, 2, 4, 3, 1, 4, 2, 1], batch=8, ctx_lo=64, ctx_hi=5000)
+    assert b.max_q_len == 4
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    g, out2, lse2, ws2 = gpu_run(b, max_q_len=0)
+    check_no_device_error(ws2, g)
+    compare(b, out2, lse2)
+    g, out3, lse3, ws3 = gpu_run(b, max_q_len=2)
+    h, _ = header(ws3, params_of(g))
+    assert h[7] == 7
+    # a prefill batch with a small bound: refused on the device, not computed as decode
+    rng = np.random.default_rng(3)
+    b = W.build_batch(rng, name="hint_prefill", kind="bf16", Hq=8, Hkv=2, d=64, page_size=64,
+                      ctx=[300, 200], q_len=[100, 1], num_pages=10)
+    g, out4, lse4, ws4 = gpu_run(b, max_q_len=1)
+    h, _ = header(ws4, params_of(g))
+    assert h[7] == 7
+
+
 def test_auto_policy_runs_each_shape():
     for b in (W.splitk_decode(q_len=1, batch=12, ctx_lo=100, ctx_hi=6000),
               W.build_batch(np.random.default_rng(5), name="uniform", kind="bf16", Hq=32, Hkv=8, d=128,
