@@ -42,8 +42,16 @@ Specification
 * U = total units; the units of Q-block q are S_q .. S_q + n_q - 1 in the
   order above (S = exclusive prefix sum of n).
 * L = force_split_units if it is > 0, else max(split_min_units, ceil(U / P)).
-  Worker w owns units [w L, min((w + 1) L, U)); there are ceil(U / L) workers.
-* n_splits(q) = 0 if n_q == 0, else floor((S_q + n_q - 1) / L) - floor(S_q / L) + 1.
+  Workers come in pairs (2k, 2k + 1), the two workgroups that share one
+  compute unit, and a pair owns the 2L units [2kL, 2kL + 2L): with
+  L0 = min(max(floor((2L w + 50) / 100), 1), 2L - 1) for the pair weight w
+  (percent; 50 gives L0 = L, the even split), worker 2k owns [2kL, 2kL + L0)
+  and worker 2k + 1 owns [2kL + L0, 2kL + 2L), each clipped to U.  Unit u
+  belongs to worker_of(u) = 2 floor(u / 2L) + (u mod 2L >= L0); there are
+  worker_of(U - 1) + 1 workers.  (The second workgroup on a compute unit is
+  issued after the first when both are ready, so it runs slower; a weight
+  above 50 gives the first one more units.)
+* n_splits(q) = 0 if n_q == 0, else worker_of(S_q + n_q - 1) - worker_of(S_q) + 1.
   Q-blocks with n_splits != 1 go, in order, into the combine list.
   Q-blocks with n_splits >= 2 get partial slots slot_base(q) = running sum of
   n_splits over earlier such Q-blocks (-1 for the others); n_slots = total.
@@ -118,9 +126,22 @@ def unit_count(desc, seq_lens, query_start_loc, Hq, Hkv, *, causal, window, expa
     return n
 
 
+def pair_split(L, pair_weight):
+    """(L0, worker_of): the pair cut of 2L units and the unit -> worker map."""
+    Lp = 2 * L
+    L0 = min(max((Lp * int(pair_weight) + 50) // 100, 1), Lp - 1)
+    return L0, (lambda u: 2 * (u // Lp) + (1 if u % Lp >= L0 else 0))
+
+
+def worker_range(w, L, L0, U):
+    """[a, b) of worker w."""
+    a = (w // 2) * 2 * L + (w % 2) * L0
+    return a, min(U, a + (2 * L - L0 if w % 2 else L0))
+
+
 def build(seq_lens, query_start_loc, *, Hq, Hkv, num_workers, split_min_units=8,
           force_split_units=0, causal=True, window=0, window_expand_to_chunk=True,
-          landmark_chunk=0, block_mask=None, block_mask_tile=128):
+          landmark_chunk=0, block_mask=None, block_mask_tile=128, pair_weight=50):
     seq_lens = [int(x) for x in seq_lens]
     qsl = [int(x) for x in query_start_loc]
     descs = q_blocks(seq_lens, qsl, Hq, Hkv)
@@ -136,11 +157,12 @@ def build(seq_lens, query_start_loc, *, Hq, Hkv, num_workers, split_min_units=8,
         L = int(force_split_units)
     else:
         L = max(int(split_min_units), -(-U // P))
+    L0, worker_of = pair_split(L, pair_weight)
     n_splits, slot_base, combine_list = [], [], []
     slots = 0
     for q, x in enumerate(n):
         S = prefix[q]
-        ns = 0 if x == 0 else (S + x - 1) // L - S // L + 1
+        ns = 0 if x == 0 else worker_of(S + x - 1) - worker_of(S) + 1
         n_splits.append(ns)
         if ns != 1:
             combine_list.append(q)
@@ -156,8 +178,8 @@ def build(seq_lens, query_start_loc, *, Hq, Hkv, num_workers, split_min_units=8,
         "n_splits": np.array(n_splits, dtype=np.int32),
         "slot_base": np.array(slot_base, dtype=np.int32),
         "combine_list": np.array(combine_list, dtype=np.int32),
-        "U": U, "P": P, "L": L, "n_qb": len(descs), "n_slots": slots,
-        "n_workers": -(-U // L) if U else 0,
+        "U": U, "P": P, "L": L, "L0": L0, "n_qb": len(descs), "n_slots": slots,
+        "n_workers": worker_of(U - 1) + 1 if U else 0,
     }
 
 

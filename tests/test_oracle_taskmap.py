@@ -11,12 +11,21 @@ def _check_invariants(tm):
     prefix, n = tm["unit_prefix"], tm["n_units"]
     assert prefix[0] == 0 and prefix[-1] == U and np.all(np.diff(prefix) == n)
     nw = tm["n_workers"]
-    assert nw == (-(-U // L) if U else 0)
+    L0 = tm["L0"]
+    assert 1 <= L0 <= 2 * L - 1
     owner_count = np.zeros(U, dtype=np.int64)
     splits = np.zeros(tm["n_qb"], dtype=np.int64)
+    # workers by direct construction: pair k covers [2kL, 2kL + 2L), the first L0 to worker 2k
+    w_of = np.empty(U, dtype=np.int64)
+    for u in range(U):
+        k, r = divmod(u, 2 * L)
+        w_of[u] = 2 * k + (r >= L0)
+    assert nw == (w_of[-1] + 1 if U else 0)
     for w in range(nw):
-        a, b = w * L, min((w + 1) * L, U)
-        assert 0 < b - a <= L
+        own = np.nonzero(w_of == w)[0]
+        a, b = own[0], own[-1] + 1
+        assert len(own) == b - a and 0 < b - a <= max(L0, 2 * L - L0)
+        assert (a, b) == taskmap.worker_range(w, L, L0, U)
         owner_count[a:b] += 1
         # Q-blocks this worker touches, by direct walk
         for q in range(tm["n_qb"]):
@@ -34,6 +43,22 @@ def _check_invariants(tm):
         else:
             assert sb[q] == -1
     assert run == tm["n_slots"] <= 2 * max(nw, 1)
+
+
+@pytest.mark.parametrize("weight", [50, 60, 99, 1])
+def test_pair_weight_split_invariants(weight):
+    b = W.splitk_decode(q_len=[1, 2, 4] * 10 + [1, 1], batch=32, ctx_lo=64, ctx_hi=4000)
+    for P in (16, 512):
+        tm = taskmap.build(b.seq_lens.numpy(), b.query_start_loc.numpy(), Hq=32, Hkv=8, num_workers=P,
+                           pair_weight=weight)
+        _check_invariants(tm)
+        L, L0 = tm["L"], tm["L0"]
+        assert L0 == min(max((2 * L * weight + 50) // 100, 1), 2 * L - 1)
+    # weight 50 is the even split: worker w owns [w L, (w + 1) L)
+    tm = taskmap.build(b.seq_lens.numpy(), b.query_start_loc.numpy(), Hq=32, Hkv=8, num_workers=64)
+    assert tm["L0"] == tm["L"]
+    for w in range(tm["n_workers"]):
+        assert taskmap.worker_range(w, tm["L"], tm["L0"], tm["U"]) == (w * tm["L"], min(tm["U"], (w + 1) * tm["L"]))
 
 
 @pytest.mark.parametrize("P", [1, 7, 64, 512])
