@@ -78,6 +78,7 @@ pa_status check_params(const pa_params* p) {
   if (p->split_mode != PA_SPLIT_DYNAMIC && p->split_mode != PA_SPLIT_STATIC) return PA_ERR_INVALID_ARG;
   if (p->static_splits < 0 || (p->split_mode == PA_SPLIT_STATIC && p->static_splits < 1)) return PA_ERR_INVALID_ARG;
   if (p->max_q_len < 0) return PA_ERR_INVALID_ARG;
+  if (p->pair_weight < 0 || p->pair_weight > 99) return PA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
   return PA_OK;
 }
@@ -373,6 +374,9 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   kp.n_qb_max = L.n_qb_max;
   kp.static_S = is_static ? P.static_splits : 0;
   kp.max_q_len = P.max_q_len;
+  // the kernel choice is needed before the launch; made here for both
+  const bool small_only = is_static || (P.max_q_len > 0 && int64_t(P.max_q_len) * kp.G <= pa::kSmallMaxRows);
+  kp.pair_w = P.pair_weight ? P.pair_weight : (small_only ? PA_PAIR_WEIGHT_SMALL : PA_PAIR_WEIGHT_GENERAL);
   char* ws = static_cast<char*>(workspace);
   kp.hdr = reinterpret_cast<int32_t*>(ws + L.header);
   kp.seq_qb_base = reinterpret_cast<int32_t*>(ws + L.seq_qb_base);
@@ -407,7 +411,6 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   const int64_t n_items = n_static_qb * P.static_splits;
   const int grid = is_static ? static_cast<int>(std::min<int64_t>(n_items, L.num_workers)) : L.num_workers;
   // the small-Q-block kernel when every Q-block is known to be small
-  const bool small_only = is_static || (P.max_q_len > 0 && int64_t(P.max_q_len) * kp.G <= pa::kSmallMaxRows);
   e = pa::launch_attention(kp, kind, grid, small_only, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (timing) (void)hipEventRecord(tc.ev[2], stream);

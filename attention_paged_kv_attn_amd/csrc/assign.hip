@@ -8,8 +8,10 @@
 // map is integer-only and must equal the CPU specification bit for bit:
 //   Q-blocks in (b, g) order, a large Q-block's token blocks zig-zag
 //   (0, n-1, 1, n-2, ...); n_units = active 64-key tiles; prefix S;
-//   L = force ? force : max(L_min, ceil(U / P)); worker w owns [wL, (w+1)L);
-//   n_splits(q) = 0 | floor((S+n-1)/L) - floor(S/L) + 1; combine list = the
+//   L = force ? force : max(L_min, ceil(U / P)); worker pair k owns
+//   [2kL, 2kL + 2L), the first L0 units to worker 2k (L0 from the pair
+//   weight, L0 = L at 50); worker_of(u) as in WorkerMap;
+//   n_splits(q) = 0 | worker_of(S+n-1) - worker_of(S) + 1; combine list = the
 //   Q-blocks with n_splits != 1; slot_base = running sum over split Q-blocks.
 #include <algorithm>
 
@@ -161,6 +163,7 @@ __device__ void assign_splits(const KParams& p, int n_qb, int* sh, int* pre) {
   }
   const int U = carry;
   const int L = p.force_L > 0 ? p.force_L : max(p.L_min, (U + p.P - 1) / p.P);
+  const WorkerMap wm{L, WorkerMap::first_len(L, p.pair_w)};
   __syncthreads();
 
   // 4. splits, combine list, partial slots
@@ -170,7 +173,7 @@ __device__ void assign_splits(const KParams& p, int n_qb, int* sh, int* pre) {
     int ns = 1;
     if (q < n_qb) {
       const int S = up[q], n = up[q + 1] - S;
-      ns = n == 0 ? 0 : (S + n - 1) / L - S / L + 1;
+      ns = n == 0 ? 0 : wm.worker_of(S + n - 1) - wm.worker_of(S) + 1;
       p.n_splits[q] = ns;
     }
     const int in_c = (q < n_qb && ns != 1) ? 1 : 0;
@@ -192,10 +195,11 @@ __device__ void assign_splits(const KParams& p, int n_qb, int* sh, int* pre) {
     p.hdr[H_NQB] = n_qb;
     p.hdr[H_NSLOTS] = s_carry;
     p.hdr[H_NCOMBINE] = over ? 0 : c_carry;
-    p.hdr[H_NWORKERS] = over ? 0 : (U ? (U + L - 1) / L : 0);
+    p.hdr[H_NWORKERS] = over ? 0 : (U ? wm.worker_of(U - 1) + 1 : 0);
     p.hdr[H_ERROR] = over ? E_SLOTS : E_NONE;
     p.hdr[H_MAXSLOTS] = p.max_slots;
-    for (int i = H_MAXSLOTS + 1; i < kHeaderInts; ++i) p.hdr[i] = 0;
+    p.hdr[H_L0] = wm.L0;
+    for (int i = H_L0 + 1; i < kHeaderInts; ++i) p.hdr[i] = 0;
   }
 }
 

@@ -1221,7 +1221,7 @@ __device__ __forceinline__ void stream_load_v(const KParams& p, StreamRec<KIND, 
 }
 
 template <int KIND, int D, bool FAST>
-__device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int b) {
+__device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap wm, int a, int b) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const KParams& p = kparams_at(pk);
   using C = Cfg<KIND, D>;
@@ -1328,7 +1328,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, int L, int a, int
     if (!first) continue;
     const QBlock x = load_qblock(p, q);
     const bool final_out = p.n_splits[q] == 1;
-    const int slot = final_out ? 0 : p.slot_base[q] + (vw - p.unit_prefix[q] / L);
+    const int slot = final_out ? 0 : p.slot_base[q] + (vw - wm.worker_of(p.unit_prefix[q]));
     for (int idx = threadIdx.x; idx < x.rows * TPR; idx += kThreads) {
       const int row = idx / TPR, d0 = (idx % TPR) * 8;
       float M = kNegInf;
@@ -1990,21 +1990,27 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
     }
   }
   const int U = p.hdr[H_U];
-  const int L = p.hdr[H_L];
+  const WorkerMap wm{p.hdr[H_L], p.hdr[H_L0]};
   const int n_workers = p.hdr[H_NWORKERS];
   if (U == 0 || n_workers == 0) return;
-  // XCD-aware: consecutive workgroup ids land on different XCDs, so give each
-  // XCD a contiguous block of workers (neighbouring units share K/V in its L2)
-  const int G8 = gridDim.x / 8;
-  const int rank = (gridDim.x % 8 == 0) ? (blockIdx.x % 8) * G8 + blockIdx.x / 8 : blockIdx.x;
+  // Workgroups b and b + grid / 2 run on one compute unit (two per unit):
+  // they are the worker pair (2k, 2k + 1), the first dispatched taking the
+  // pair's first run.  Pairs are spread XCD-aware: consecutive workgroup ids
+  // land on different XCDs, so each XCD gets a contiguous block of pairs
+  // (neighbouring units share K/V in its L2).
+  int rank = blockIdx.x;
+  if ((gridDim.x & 15) == 0) {
+    const int half = gridDim.x >> 1, b = blockIdx.x % half;
+    rank = 2 * ((b & 7) * (half >> 3) + (b >> 3)) + (blockIdx.x >= half ? 1 : 0);
+  }
   const int n_qb = p.hdr[H_NQB];
   DirectStage ds;                                  // large segments' K/V addressing, kept across segments
   ds.cur_b = -1;
   ds.cur_g = -1;
   ds.pbase = -(1 << 30);
   for (int vw = rank; vw < n_workers; vw += gridDim.x) {
-    int a = vw * L;
-    const int b_end = min(a + L, U);
+    int a = wm.start(vw);
+    const int b_end = min(a + wm.size(vw), U);
     int q = find_qblock(p, 0, n_qb - 1, a, threadIdx.x & 63);
     while (a < b_end && q < n_qb) {
       const int S = p.unit_prefix[q], nq = p.unit_prefix[q + 1] - S;
@@ -2021,7 +2027,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
           ++qq;
         }
         run_end = wave_uniform(run_end);
-        small_range<KIND, D, FAST>(pk, vw, L, a, run_end);
+        small_range<KIND, D, FAST>(pk, vw, wm, a, run_end);
         a = run_end;
         while (q < n_qb && p.unit_prefix[q + 1] <= a) ++q;
         continue;
@@ -2029,7 +2035,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
       int t_lo = 0, t_hi = 0;
       qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, t_lo, t_hi);
       const bool final_out = p.n_splits[q] == 1;
-      const int slot = final_out ? 0 : p.slot_base[q] + (vw - S / L);
+      const int slot = final_out ? 0 : p.slot_base[q] + (vw - wm.worker_of(S));
       if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
       else if constexpr (SMALL) {
         if (threadIdx.x == 0) p.hdr[H_ERROR] = E_QLEN_HINT;

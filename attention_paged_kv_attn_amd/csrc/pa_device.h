@@ -25,7 +25,7 @@ constexpr int kMaskListCap = 1024;   // active-tile list entries kept in LDS at 
 
 enum HeaderField {
   H_U = 0, H_P = 1, H_L = 2, H_NQB = 3, H_NSLOTS = 4, H_NCOMBINE = 5, H_NWORKERS = 6,
-  H_ERROR = 7, H_MAXSLOTS = 8
+  H_ERROR = 7, H_MAXSLOTS = 8, H_L0 = 9
 };
 
 enum DevError { E_NONE = 0, E_QSL = 1, E_QLEN = 2, E_SLOTS = 3, E_PAGE = 5, E_STATIC_ROWS = 6, E_QLEN_HINT = 7 };
@@ -55,6 +55,7 @@ struct KParams {
   int32_t P, L_min, force_L, max_slots, n_qb_max;
   int32_t static_S;  // > 0: static split, every Q-block cut into static_S equal tile ranges (no task map)
   int32_t max_q_len; // > 0: the caller's bound on every q_len (checked by Assign)
+  int32_t pair_w;    // percent of a worker pair's 2L units given to its first worker
   // workspace
   int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
   int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;
@@ -98,6 +99,23 @@ __device__ __forceinline__ bool mask_union(const KParams& p, int b, int g, int p
       if (base[hm * p.bm_sh + qt * p.bm_sq]) return true;
   return false;
 }
+
+// The workers' unit ranges: pairs (2k, 2k + 1) share 2L units, the first
+// L0 to worker 2k (L0 = L is the even split).
+struct WorkerMap {
+  int L, L0;
+  __device__ __forceinline__ static int first_len(int L, int pair_w) {
+    const int Lp = 2 * L;
+    return min(max((Lp * pair_w + 50) / 100, 1), Lp - 1);
+  }
+  __device__ __forceinline__ int worker_of(int u) const {
+    const int Lp = 2 * L;
+    const int k = u / Lp;
+    return 2 * k + (u - k * Lp >= L0 ? 1 : 0);
+  }
+  __device__ __forceinline__ int start(int w) const { return (w >> 1) * 2 * L + (w & 1) * L0; }
+  __device__ __forceinline__ int size(int w) const { return (w & 1) ? 2 * L - L0 : L0; }
+};
 
 // Decoded Q-block: rows are (token t0 + r / G, head g * G + r % G).
 struct QBlock {

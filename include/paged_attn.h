@@ -130,7 +130,15 @@ typedef struct pa_params {
                                    prefill path runs (faster decode).  A sequence longer than
                                    the bound is device error PA_DEV_QLEN_HINT (outputs then
                                    unspecified). */
+  int32_t pair_weight;          /* 1..99: percent of each worker pair's 2L units given to its
+                                   first worker (the workgroup dispatched first onto a compute
+                                   unit, which the hardware favours); 50 is the even split.
+                                   0 = PA_PAIR_WEIGHT_SMALL with the small-Q-block kernel,
+                                   PA_PAIR_WEIGHT_GENERAL otherwise (measured on MI355X) */
 } pa_params;
+
+#define PA_PAIR_WEIGHT_SMALL 60
+#define PA_PAIR_WEIGHT_GENERAL 50
 
 /* How the keys of each Q-block are cut into splits.
  *  PA_SPLIT_DYNAMIC  Assign builds a balanced task map on the device from the

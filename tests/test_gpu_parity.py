@@ -76,18 +76,27 @@ def check_no_device_error(ws, g, **kw):
     return h
 
 
-def oracle_taskmap(b, P, force=0):
+def effective_pair_weight(b, weight=0):
+    """The library's pair weight for a run_batch call (which states the batch's max_q_len)."""
+    if weight:
+        return weight
+    small = b.max_q_len * (b.num_q_heads // b.num_kv_heads) <= 16
+    return B.PA_PAIR_WEIGHT_SMALL if small else B.PA_PAIR_WEIGHT_GENERAL
+
+
+def oracle_taskmap(b, P, force=0, weight=0):
     return taskmap.build(b.seq_lens.numpy(), b.query_start_loc.numpy(), Hq=b.num_q_heads,
                          Hkv=b.num_kv_heads, num_workers=P, split_min_units=8, force_split_units=force,
+                         pair_weight=effective_pair_weight(b, weight),
                          causal=b.causal, window=b.window, window_expand_to_chunk=b.window_expand_to_chunk,
                          landmark_chunk=b.landmark_chunk,
                          block_mask=None if b.block_mask is None else b.block_mask.numpy(),
                          block_mask_tile=b.block_mask_tile)
 
 
-def slots_for(b, P, force):
+def slots_for(b, P, force, weight=0):
     """Partial slots a forced split needs (the default 2 P covers natural splits)."""
-    return max(1, oracle_taskmap(b, P, force)["n_slots"]) if force else 0
+    return max(1, oracle_taskmap(b, P, force, weight)["n_slots"]) if force else 0
 
 
 def sample_rows(total_q, k, seed=0, must=()):
@@ -113,14 +122,16 @@ def test_device_info():
     lambda: W.sparse_prefill(kind="bf16", seq_len=1024),
     lambda: W.sliding_window(seq_len=1500, window=512),
 ], ids=["tiny", "decode", "mtp_mix", "hybrid", "sparse", "window"])
-@pytest.mark.parametrize("workers,force", [(0, 0), (7, 0), (64, 0), (37, 1), (5, 3)])
-def test_taskmap_bit_exact(make, workers, force):
+@pytest.mark.parametrize("workers,force,weight", [(0, 0, 0), (0, 0, 73), (7, 0, 0), (64, 0, 35), (37, 1, 0),
+                                                  (5, 3, 90)])
+def test_taskmap_bit_exact(make, workers, force, weight):
     b = make()
     info = B.paged_attn_device_info(0)
     P = workers or info["default_workers"]
-    ref = oracle_taskmap(b, P, force)
-    slots = slots_for(b, P, force)
-    g, out, lse, ws = gpu_run(b, num_workers=workers, force_split_units=force, max_partial_slots=slots)
+    ref = oracle_taskmap(b, P, force, weight)
+    slots = slots_for(b, P, force, weight)
+    g, out, lse, ws = gpu_run(b, num_workers=workers, force_split_units=force, max_partial_slots=slots,
+                              pair_weight=weight)
     params = params_of(g, num_workers=workers, force_split_units=force, max_partial_slots=slots)
     h, lay = header(ws, params)
     wsc = ws.cpu()
@@ -131,8 +142,8 @@ def test_taskmap_bit_exact(make, workers, force):
         return a.reshape(-1, width) if width > 1 else a
 
     assert h[7] == 0
-    assert (h[0], h[1], h[2], h[3], h[4], h[5], h[6]) == (
-        ref["U"], P, ref["L"], n, ref["n_slots"], len(ref["combine_list"]), ref["n_workers"])
+    assert (h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[9]) == (
+        ref["U"], P, ref["L"], n, ref["n_slots"], len(ref["combine_list"]), ref["n_workers"], ref["L0"])
     desc = arr(lay.qb_desc, n, 8)
     assert np.array_equal(desc[:, :4], ref["desc"])
     qsl, ctx = b.query_start_loc.numpy(), b.seq_lens.numpy()
