@@ -47,13 +47,13 @@ class pa_params(ctypes.Structure):
         (n, ctypes.c_int32) for n in (
             "causal", "window", "window_expand_to_chunk", "landmark_chunk", "block_mask_tile",
             "num_workers", "split_min_units", "force_split_units", "max_partial_slots", "flags",
-            "split_mode", "static_splits", "max_q_len", "pair_weight")]
+            "split_mode", "static_splits", "max_q_len", "pair_weight", "fused_combine")]
 
 
 class pa_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "header", "seq_qb_base", "qb_desc", "unit_prefix", "n_splits", "slot_base", "combine_list",
-        "partial_lse", "partial_o", "total")] + [
+        "done", "partial_lse", "partial_o", "total")] + [
         ("n_qb_max", ctypes.c_int32), ("max_slots", ctypes.c_int32), ("num_workers", ctypes.c_int32)]
 
 
@@ -145,7 +145,8 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
                 max_pages_per_seq, total_q, softmax_scale, block_table_stride=None, causal=True,
                 window=0, window_expand_to_chunk=True, landmark_chunk=0, block_mask_tile=128,
                 num_workers=0, split_min_units=0, force_split_units=0, max_partial_slots=0,
-                split_mode=PA_SPLIT_DYNAMIC, static_splits=0, max_q_len=0, pair_weight=0) -> pa_params:
+                split_mode=PA_SPLIT_DYNAMIC, static_splits=0, max_q_len=0, pair_weight=0,
+                fused_combine=0) -> pa_params:
     p = pa_params()
     p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
     p.page_size, p.num_pages, p.max_pages_per_seq = page_size, num_pages, max_pages_per_seq
@@ -159,6 +160,7 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
     p.split_mode, p.static_splits = split_mode, static_splits
     p.max_q_len = max_q_len
     p.pair_weight = pair_weight
+    p.fused_combine = int(fused_combine)
     return p
 
 
@@ -238,7 +240,7 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    block_mask_tile: int = 128, num_workers: int = 0, split_min_units: int = 0,
                    force_split_units: int = 0, max_partial_slots: int = 0, split: str = "dynamic",
                    static_splits: int = 0, max_q_len: int = 0, pair_weight: int = 0,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
+                   fused_combine: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Run the library on torch tensors; returns (out, lse, workspace).
 
     q [total_q, Hq, d]; k_cache/v_cache NHD [pages, page_size, Hkv, d] or HND
@@ -267,7 +269,8 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                          window_expand_to_chunk=window_expand_to_chunk, landmark_chunk=landmark_chunk,
                          block_mask_tile=block_mask_tile, num_workers=num_workers,
                          split_min_units=split_min_units, force_split_units=force_split_units,
-                         max_partial_slots=max_partial_slots, max_q_len=max_q_len, pair_weight=pair_weight)
+                         max_partial_slots=max_partial_slots, max_q_len=max_q_len, pair_weight=pair_weight,
+                         fused_combine=fused_combine)
     if split == "auto":
         params.split_mode, params.static_splits = paged_attn_plan_split(params, seq_lens, query_start_loc,
                                                                         block_mask is not None)

@@ -79,6 +79,7 @@ pa_status check_params(const pa_params* p) {
   if (p->static_splits < 0 || (p->split_mode == PA_SPLIT_STATIC && p->static_splits < 1)) return PA_ERR_INVALID_ARG;
   if (p->max_q_len < 0) return PA_ERR_INVALID_ARG;
   if (p->pair_weight < 0 || p->pair_weight > 99) return PA_ERR_INVALID_ARG;
+  if (p->fused_combine != 0 && p->fused_combine != 1) return PA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
   return PA_OK;
 }
@@ -105,6 +106,7 @@ pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   L->n_splits = off;      off = align256(off + size_t(n_qb_max) * 4);
   L->slot_base = off;     off = align256(off + size_t(n_qb_max) * 4);
   L->combine_list = off;  off = align256(off + size_t(n_qb_max) * 4);
+  L->done = off;          off = align256(off + size_t(n_qb_max) * 4);
   L->partial_lse = off;   off = align256(off + size_t(max_slots) * pa::kLargeRows * 4);
   L->partial_o = off;     off = align256(off + size_t(max_slots) * pa::kLargeRows * p->head_dim * 4);
   L->total = off;
@@ -377,6 +379,7 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   // the kernel choice is needed before the launch; made here for both
   const bool small_only = is_static || (P.max_q_len > 0 && int64_t(P.max_q_len) * kp.G <= pa::kSmallMaxRows);
   kp.pair_w = P.pair_weight ? P.pair_weight : (small_only ? PA_PAIR_WEIGHT_SMALL : PA_PAIR_WEIGHT_GENERAL);
+  kp.fused = P.fused_combine ? 1 : 0;
   char* ws = static_cast<char*>(workspace);
   kp.hdr = reinterpret_cast<int32_t*>(ws + L.header);
   kp.seq_qb_base = reinterpret_cast<int32_t*>(ws + L.seq_qb_base);
@@ -385,6 +388,7 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   kp.n_splits = reinterpret_cast<int32_t*>(ws + L.n_splits);
   kp.slot_base = reinterpret_cast<int32_t*>(ws + L.slot_base);
   kp.combine_list = reinterpret_cast<int32_t*>(ws + L.combine_list);
+  kp.done = reinterpret_cast<int32_t*>(ws + L.done);
   kp.part_lse = reinterpret_cast<float*>(ws + L.partial_lse);
   kp.part_o = reinterpret_cast<float*>(ws + L.partial_o);
 
@@ -414,7 +418,7 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   e = pa::launch_attention(kp, kind, grid, small_only, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (timing) (void)hipEventRecord(tc.ev[2], stream);
-  if (!is_static || P.static_splits > 1) {
+  if (!P.fused_combine && (!is_static || P.static_splits > 1)) {
     const int cgrid = is_static ? static_cast<int>(std::min<int64_t>(n_static_qb, L.num_workers)) : L.num_workers;
     e = pa::launch_combine(kp, kind == pa::KIND_F32, cgrid, stream);
     if (e != hipSuccess) return hip_fail(e);

@@ -175,6 +175,7 @@ __device__ void assign_splits(const KParams& p, int n_qb, int* sh, int* pre) {
       const int S = up[q], n = up[q + 1] - S;
       ns = n == 0 ? 0 : wm.worker_of(S + n - 1) - wm.worker_of(S) + 1;
       p.n_splits[q] = ns;
+      p.done[q] = 0;
     }
     const int in_c = (q < n_qb && ns != 1) ? 1 : 0;
     const int in_s = (q < n_qb && ns >= 2) ? ns : 0;
@@ -283,7 +284,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_end_kernel(KParams p) {
 
 // Static split: no task map, only the header (error word cleared, sizes for
 // inspection) written before the attention kernel.
-__global__ __launch_bounds__(64) void static_begin_kernel(KParams p) {
+__global__ __launch_bounds__(256) void static_begin_kernel(KParams p) {
+  for (int q = threadIdx.x; q < p.B * p.Hkv; q += blockDim.x) p.done[q] = 0;
   if (threadIdx.x == 0) {
     const int n_qb = p.B * p.Hkv;
     p.hdr[H_U] = 0;
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(64) void static_begin_kernel(KParams p) {
 }
 
 hipError_t launch_static_begin(const KParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(static_begin_kernel, dim3(1), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(static_begin_kernel, dim3(1), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -36,6 +36,7 @@
 // ballot + mbcnt prefix into an LDS list ("Triton-TLE ...", §2.1).
 #include <type_traits>
 
+#include "combine_core.h"
 #include "pa_device.h"
 
 namespace pa {
@@ -619,10 +620,18 @@ __device__ __forceinline__ void write_row(const KParams& p, const QBlock& x, int
       if (h == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
     } else {
       float* o = p.part_o + ((int64_t)slot * kLargeRows + r) * D;
+      if (p.fused) {
 #pragma unroll
-      for (int md = 0; md < MD; ++md)
-        *reinterpret_cast<f32x4*>(o + out_dim<KIND, D, true>(h, 0, md)) = acc[md] * inv_l;
-      if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) store_coherent(o + out_dim<KIND, D, true>(h, 0, md) + i, acc[md][i] * inv_l);
+        if (h == 0) store_coherent(p.part_lse + slot * kLargeRows + r, lse);
+      } else {
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+          *reinterpret_cast<f32x4*>(o + out_dim<KIND, D, true>(h, 0, md)) = acc[md] * inv_l;
+        if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+      }
     }
     return;
   }
@@ -653,11 +662,19 @@ __device__ __forceinline__ void write_row(const KParams& p, const QBlock& x, int
     if (h == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
   } else {
     float* o = p.part_o + ((int64_t)slot * kLargeRows + r) * D;
+    if (p.fused) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int md = 0; md < MD; ++md) o[out_dim<KIND, D>(h, j, md)] = acc[md][j] * inv_l;
-    if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+        for (int md = 0; md < MD; ++md) store_coherent(o + out_dim<KIND, D>(h, j, md), acc[md][j] * inv_l);
+      if (h == 0) store_coherent(p.part_lse + slot * kLargeRows + r, lse);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[out_dim<KIND, D>(h, j, md)] = acc[md][j] * inv_l;
+      if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+    }
   }
 }
 
@@ -924,6 +941,31 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
   small_pv<KIND, D>(r, sc, vsc, st);
 }
 
+// ---------------------------------------------------------------------------
+// fused combine ("Triton-TLE rewrite of Tencent HPC-Ops Attention", §3.3: each
+// split publishes its partial state and a completion counter tells the last
+// one to merge; the AMD counterpart of the page's cluster merge is a
+// device-scope counter per Q-block).  Called by the whole workgroup after it
+// wrote its partial of split Q-block q (device-coherent stores, complete
+// before the counter moves); the workgroup that brings the counter to ns
+// merges all ns partials (device-coherent loads) and writes the output rows.
+// No workgroup waits on another.
+// ---------------------------------------------------------------------------
+template <int KIND, int D>
+__device__ void finish_split(const KParams& p, int q, const QBlock& x, int ns, int sb) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int last;
+  // the partial went out with device-coherent stores: once they are complete
+  // (all of this thread's memory operations), the counter may move
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(p.done + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+  __syncthreads();
+  if (last) merge_qblock<D, KIND == KIND_F32, true>(p, x, ns, sb, reinterpret_cast<MergeState*>(smem));
+  __syncthreads();
+}
+
 // One tile in flight per wave: the second wave on each SIMD (two workgroups
 // per compute unit) computes while this one waits for its loads.
 template <int KIND, int D, bool FAST>
@@ -1045,9 +1087,14 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
       if (d0 == 0) p.lse[tk * p.l_st + hd * p.l_sh] = lse;
     } else {
       float* dst = p.part_o + ((int64_t)slot * kLargeRows + row) * D + d0;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-      if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+      if (p.fused) {
+        for (int i = 0; i < 8; ++i) store_coherent(dst + i, o[i] * inv);
+        if (d0 == 0) store_coherent(p.part_lse + slot * kLargeRows + row, lse);
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+      }
     }
   }
   __syncthreads();
@@ -1361,13 +1408,34 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
         if (d0 == 0) p.lse[tk * p.l_st + hd * p.l_sh] = lse;
       } else {
         float* dst = p.part_o + ((int64_t)slot * kLargeRows + row) * D + d0;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-        if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+        if (p.fused) {
+          for (int i = 0; i < 8; ++i) store_coherent(dst + i, o[i] * inv);
+          if (d0 == 0) store_coherent(p.part_lse + slot * kLargeRows + row, lse);
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+          if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+        }
       }
     }
   }
   __syncthreads();
+  if (p.fused) {
+    // the Q-block of each partial written above (tags lie past the merge scratch,
+    // but are read before any merge anyway)
+    int pend[SL::PIECES];
+#pragma unroll
+    for (int k = 0; k < SL::PIECES; ++k) {
+      const int q = tags[k];
+      bool first = q >= 0;
+      for (int j = 0; j < k; ++j) first = first && tags[j] != q;
+      pend[k] = first && p.n_splits[q] != 1 ? q : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < SL::PIECES; ++k)
+      if (pend[k] >= 0) finish_split<KIND, D>(p, pend[k], load_qblock(p, pend[k]), p.n_splits[pend[k]],
+                                               p.slot_base[pend[k]]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1965,6 +2033,7 @@ __device__ __forceinline__ void static_items(uint64_t pk) {
     const bool final_out = sp.ns == 1;
     small_segment<KIND, D, FAST>(pk, x, sp.t_lo, sp.t_lo + sp.n - 1, u0, min(sp.n, u0 + sp.c), final_out,
                                  final_out ? 0 : it);
+    if (!final_out && p.fused) finish_split<KIND, D>(p, q, x, sp.ns, q * S);
   }
 }
 
@@ -1992,6 +2061,15 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   const int U = p.hdr[H_U];
   const WorkerMap wm{p.hdr[H_L], p.hdr[H_L0]};
   const int n_workers = p.hdr[H_NWORKERS];
+  if (p.fused) {
+    // Q-blocks without a unit (no visible key): their rows, spread over the grid
+    const int n_combine = p.hdr[H_NCOMBINE];
+    for (int i = blockIdx.x; i < n_combine; i += gridDim.x) {
+      const int q = p.combine_list[i];
+      if (p.n_splits[q] == 0)
+        merge_qblock<D, KIND == KIND_F32>(p, load_qblock(p, q), 0, 0, reinterpret_cast<MergeState*>(smem));
+    }
+  }
   if (U == 0 || n_workers == 0) return;
   // Workgroups b and b + grid / 2 run on one compute unit (two per unit):
   // they are the worker pair (2k, 2k + 1), the first dispatched taking the
@@ -2039,9 +2117,13 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
       if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
       else if constexpr (SMALL) {
         if (threadIdx.x == 0) p.hdr[H_ERROR] = E_QLEN_HINT;
+        a = S + u1;
+        ++q;
+        continue;
       } else {
         large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot, ds);
       }
+      if (!final_out && p.fused) finish_split<KIND, D>(p, q, x, p.n_splits[q], p.slot_base[q]);
       a = S + u1;
       ++q;
     }

@@ -56,9 +56,11 @@ struct KParams {
   int32_t static_S;  // > 0: static split, every Q-block cut into static_S equal tile ranges (no task map)
   int32_t max_q_len; // > 0: the caller's bound on every q_len (checked by Assign)
   int32_t pair_w;    // percent of a worker pair's 2L units given to its first worker
+  int32_t fused;     // 1: the last workgroup to finish a split Q-block merges it (no Combine launch)
   // workspace
   int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
   int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;
+  int32_t* done;     // per Q-block: split pieces finished (fused combine)
   float* part_lse; float* part_o;
 };
 

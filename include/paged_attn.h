@@ -135,6 +135,12 @@ typedef struct pa_params {
                                    unit, which the hardware favours); 50 is the even split.
                                    0 = PA_PAIR_WEIGHT_SMALL with the small-Q-block kernel,
                                    PA_PAIR_WEIGHT_GENERAL otherwise (measured on MI355X) */
+  int32_t fused_combine;        /* 0: a Combine kernel of its own after the attention kernel;
+                                   1: fused Combine — the workgroup that finishes a split
+                                   Q-block's last piece merges its partials (a per-Q-block
+                                   counter in the workspace, partials through device-coherent
+                                   accesses), one launch fewer.  Measured slower on MI355X
+                                   (the merges land on the kernel's tail), so not the default */
 } pa_params;
 
 #define PA_PAIR_WEIGHT_SMALL 60
@@ -171,6 +177,7 @@ typedef struct pa_workspace_layout {
   size_t n_splits;        /* int32[n_qb_max] */
   size_t slot_base;       /* int32[n_qb_max], -1 when not split */
   size_t combine_list;    /* int32[n_qb_max] */
+  size_t done;            /* int32[n_qb_max]: finished pieces per split Q-block (fused Combine) */
   size_t partial_lse;     /* float[max_slots][128] */
   size_t partial_o;       /* float[max_slots][128][head_dim] */
   size_t total;           /* bytes needed */
@@ -198,11 +205,11 @@ typedef enum pa_device_error {
 } pa_device_error;
 
 /*
- * paged_attn_fwd — the whole forward pass, enqueued on `stream` as three
- * launches: Assign (one workgroup builds the task map in the workspace),
- * the persistent split-K attention kernel (P workgroups), Combine; with
- * PA_SPLIT_STATIC, a one-thread header reset, the attention kernel and
- * (S > 1) Combine.
+ * paged_attn_fwd — the whole forward pass, enqueued on `stream`: Assign (one
+ * workgroup builds the task map in the workspace), then the persistent
+ * split-K attention kernel (P workgroups), then Combine (or, with
+ * fused_combine, the last workgroup on each split Q-block merges it);
+ * with PA_SPLIT_STATIC a one-workgroup header reset replaces Assign.
  *
  *  q            [total_q, Hq, d], dtype f32 | bf16 | e4m3; strides for the
  *               first two dims are free (d contiguous).
