@@ -306,6 +306,48 @@ def splitk_decode(q_len=1, kv_layout: str = "NHD", seed: int = 2, batch: int = 6
                        q_quant=q_quant if kind == "e4m3" else "tensor")
 
 
+def replay_variants(n: int = 4, batch: int = 16, total_q: int = 32, max_q_len: int = 4, ctx_lo: int = 64,
+                    ctx_hi: int = 6000, seed: int = 9, kind: str = "bf16"):
+    """Batches that share one set of buffers (Q, K/V caches, block table,
+    seq_lens, query_start_loc of fixed shapes) but differ in their contents:
+    each variant draws new context lengths, new q_len (summing to the same
+    total_q, zeros allowed) and a new page permutation over the same cache,
+    as a serving loop replaying one captured graph would.  Returns the list
+    of PagedBatch (variant 0 owns the buffers' initial contents)."""
+    rng = np.random.default_rng(seed)
+    page_size, Hq, Hkv, d = 64, 32, 8, 128
+    max_pages = -(-ctx_hi // page_size)
+    num_pages = batch * max_pages
+    base = None
+    out = []
+    for v in range(n):
+        # q_len: total_q spread over the sequences, each at most max_q_len
+        ql = np.zeros(batch, dtype=np.int64)
+        for _ in range(total_q):
+            free = np.nonzero(ql < max_q_len)[0]
+            ql[rng.choice(free)] += 1
+        ctx = np.maximum(decode_ctx_lengths(rng, batch, ctx_lo, ctx_hi), ql)
+        if base is None:
+            base = build_batch(rng, name="replay_v0", kind=kind, Hq=Hq, Hkv=Hkv, d=d, page_size=page_size,
+                               ctx=[max_pages * page_size] * batch, q_len=[total_q // batch] * batch,
+                               num_pages=num_pages, poison=False, quant_mode="tensor" if kind == "e4m3" else None)
+        perm = rng.permutation(num_pages)
+        bt = np.full((batch, max_pages), -1, dtype=np.int32)
+        off = 0
+        for b in range(batch):
+            npg = -(-int(ctx[b]) // page_size)
+            bt[b, :npg] = perm[off:off + npg]
+            off += npg
+        qsl = np.zeros(batch + 1, dtype=np.int32)
+        qsl[1:] = np.cumsum(ql)
+        kw = dict(base.__dict__)
+        kw.update(name=f"replay_v{v}", block_table=torch.from_numpy(bt),
+                  seq_lens=torch.from_numpy(ctx.astype(np.int32)), query_start_loc=torch.from_numpy(qsl),
+                  max_q_len=max_q_len)
+        out.append(PagedBatch(**kw))
+    return out
+
+
 def uniform_decode(ctx: int = 4096, batch: int = 64, q_len: int = 1, seed: int = 6, poison: bool = True,
                    kind: str = "bf16") -> PagedBatch:
     """Decode batch whose sequences all hold `ctx` keys (Llama-3.1-8B heads,

@@ -148,10 +148,38 @@ def split_kw(spec, g):
     raise ValueError(spec)
 
 
+def time_graph(g, kw, steps, warmup):
+    """The step captured once in a HIP graph, then replayed: ms per replay."""
+    import torch
+    from attention_paged_kv_attn_amd import binding as B
+    out, lse, ws = B.run_batch(g, **kw)
+    for _ in range(warmup):
+        B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def time_workload(batch, steps, warmup, split=None):
     import torch
     from attention_paged_kv_attn_amd import binding as B
     g = batch.to("cuda:0")
+    if split and split.endswith("+graph"):
+        kw = split_kw(split[:-len("+graph")] or None, g)
+        ms = time_graph(g, kw, steps, warmup)
+        return ms, {"assign": float("nan"), "attention": float("nan"), "combine": float("nan")}, None
     kw = split_kw(split, g)
     out, lse, ws = B.run_batch(g, **kw)      # allocates outputs + workspace once
     torch.cuda.synchronize()
@@ -230,7 +258,8 @@ def _full_decode_128k():
 
 
 def leg(name, steps, warmup):
-    """name is a workload, optionally '@dynamic', '@auto' or '@static<S>'."""
+    """name is a workload, optionally '@dynamic', '@auto' or '@static<S>', and
+    '+graph' to time replays of the step captured in a HIP graph."""
     name, _, split = name.partition("@")
     log(f"generating {name}")
     batch = WORKLOADS[name]()
@@ -450,11 +479,12 @@ def main():
     also = []
     for name in [x for x in args.extra.split(",") if x]:
         eb, eby, efl, ems, ekms = leg(name, max(5, args.steps // 2), args.warmup)
-        also.append({"workload": name, "ms_per_step": round(ems, 5),
-                     "gbs_step": round(eby / (ems * 1e-3) / 1e9, 1),
-                     "tflops_attention": round(efl / (ekms["attention"] * 1e-3) / 1e12, 2),
-                     "gbs_attention": round(eby / (ekms["attention"] * 1e-3) / 1e9, 1),
-                     "kernels_ms": {k: round(v, 5) for k, v in ekms.items()}})
+        entry = {"workload": name, "ms_per_step": round(ems, 5), "gbs_step": round(eby / (ems * 1e-3) / 1e9, 1)}
+        if ekms["attention"] == ekms["attention"]:          # per-kernel times exist (not a graph replay)
+            entry.update({"tflops_attention": round(efl / (ekms["attention"] * 1e-3) / 1e12, 2),
+                          "gbs_attention": round(eby / (ekms["attention"] * 1e-3) / 1e9, 1),
+                          "kernels_ms": {k: round(v, 5) for k, v in ekms.items()}})
+        also.append(entry)
         del eb
     if also:
         result["also"] = also

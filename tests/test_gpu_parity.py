@@ -503,6 +503,47 @@ def test_fused_combine_equals_combine_kernel(make, kw):
         compare(b, o1, l1)
 
 
+@pytest.mark.parametrize("split", ["dynamic", "static"])
+def test_graph_replay_with_changing_batch(split):
+    """One forward call captured in a HIP graph, replayed after the batch
+    metadata (seq_lens, query_start_loc, block table) is rewritten in place:
+    every replay equals an eager call on the same data bit for bit and
+    matches the oracle; eager work and synchronisation run between replays."""
+    vs = W.replay_variants()
+    g0 = vs[0].to(DEV)
+    P = B.paged_attn_device_info(0)["default_workers"]
+    bt, sl, qsl = g0.block_table.clone(), g0.seq_lens.clone(), g0.query_start_loc.clone()
+    kw = dict(softmax_scale=g0.softmax_scale, kv_layout=g0.kv_layout, causal=True, max_q_len=4, num_workers=P)
+    if split == "static":
+        kw.update(split="static", static_splits=4)
+    out = torch.empty((g0.total_q, g0.num_q_heads, g0.head_dim), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((g0.total_q, g0.num_q_heads), dtype=torch.float32, device=DEV)
+    _, _, ws = B.paged_attn_fwd(g0.q, g0.k_cache, g0.v_cache, bt, sl, qsl, None, g0.scales, out, lse, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.paged_attn_fwd(g0.q, g0.k_cache, g0.v_cache, bt, sl, qsl, None, g0.scales, out, lse, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    ws_eager = torch.empty_like(ws)
+    for rep in range(2):
+        for v in vs[1:] + vs[:1]:
+            bt.copy_(v.block_table.to(DEV))
+            sl.copy_(v.seq_lens.to(DEV))
+            qsl.copy_(v.query_start_loc.to(DEV))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            o_r, l_r = out.clone(), lse.clone()
+            check_no_device_error(ws, g0)
+            o_e, l_e, _ = B.paged_attn_fwd(g0.q, g0.k_cache, g0.v_cache, bt, sl, qsl, None, g0.scales,
+                                           workspace=ws_eager, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(o_r.view(torch.int16), o_e.view(torch.int16))
+            assert torch.equal(l_r.view(torch.int32), l_e.view(torch.int32))
+            if rep == 0:
+                compare(v, o_r, l_r)
+
+
 def test_auto_policy_runs_each_shape():
     for b in (W.splitk_decode(q_len=1, batch=12, ctx_lo=100, ctx_hi=6000),
               W.build_batch(np.random.default_rng(5), name="uniform", kind="bf16", Hq=32, Hkv=8, d=128,
