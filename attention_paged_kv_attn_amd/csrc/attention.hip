@@ -2071,15 +2071,19 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
     }
   }
   if (U == 0 || n_workers == 0) return;
-  // Workgroups b and b + grid / 2 run on one compute unit (two per unit):
-  // they are the worker pair (2k, 2k + 1), the first dispatched taking the
-  // pair's first run.  Pairs are spread XCD-aware: consecutive workgroup ids
-  // land on different XCDs, so each XCD gets a contiguous block of pairs
-  // (neighbouring units share K/V in its L2).
+  // XCD-aware numbering: consecutive workgroup ids land on different XCDs, so
+  // each XCD gets a contiguous block of workers (neighbouring units share K/V
+  // in its L2).  The small-Q-block kernel also pairs workers per compute unit:
+  // workgroups b and b + grid / 2 run on one unit (two per unit) and become
+  // the worker pair (2k, 2k + 1), the first dispatched taking the pair's
+  // first (weighted) run.  The general kernel keeps workers r and r + grid / 16
+  // on one unit (measured faster for prefill and sliding-window batches).
   int rank = blockIdx.x;
-  if ((gridDim.x & 15) == 0) {
+  if (SMALL && (gridDim.x & 15) == 0) {
     const int half = gridDim.x >> 1, b = blockIdx.x % half;
     rank = 2 * ((b & 7) * (half >> 3) + (b >> 3)) + (blockIdx.x >= half ? 1 : 0);
+  } else if (gridDim.x % 8 == 0) {
+    rank = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   }
   const int n_qb = p.hdr[H_NQB];
   DirectStage ds;                                  // large segments' K/V addressing, kept across segments

@@ -99,7 +99,7 @@ def algorithmic_bytes(batch, keys_per_head):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("attention.hip", "pa_device.h"):
+    for f in ("attention.hip", "pa_device.h", "combine_core.h"):
         with open(os.path.join(ROOT, "attention_paged_kv_attn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
