@@ -47,7 +47,7 @@ class pa_params(ctypes.Structure):
         (n, ctypes.c_int32) for n in (
             "causal", "window", "window_expand_to_chunk", "landmark_chunk", "block_mask_tile",
             "num_workers", "split_min_units", "force_split_units", "max_partial_slots", "flags",
-            "split_mode", "static_splits", "max_q_len", "pair_weight", "fused_combine")]
+            "split_mode", "static_splits", "max_q_len", "min_q_len", "pair_weight", "fused_combine")]
 
 
 class pa_workspace_layout(ctypes.Structure):
@@ -145,7 +145,7 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
                 max_pages_per_seq, total_q, softmax_scale, block_table_stride=None, causal=True,
                 window=0, window_expand_to_chunk=True, landmark_chunk=0, block_mask_tile=128,
                 num_workers=0, split_min_units=0, force_split_units=0, max_partial_slots=0,
-                split_mode=PA_SPLIT_DYNAMIC, static_splits=0, max_q_len=0, pair_weight=0,
+                split_mode=PA_SPLIT_DYNAMIC, static_splits=0, max_q_len=0, min_q_len=0, pair_weight=0,
                 fused_combine=0) -> pa_params:
     p = pa_params()
     p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
@@ -159,6 +159,7 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
     p.max_partial_slots, p.flags = max_partial_slots, 0
     p.split_mode, p.static_splits = split_mode, static_splits
     p.max_q_len = max_q_len
+    p.min_q_len = min_q_len
     p.pair_weight = pair_weight
     p.fused_combine = int(fused_combine)
     return p
@@ -239,7 +240,7 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    window: int = 0, window_expand_to_chunk: bool = True, landmark_chunk: int = 0,
                    block_mask_tile: int = 128, num_workers: int = 0, split_min_units: int = 0,
                    force_split_units: int = 0, max_partial_slots: int = 0, split: str = "dynamic",
-                   static_splits: int = 0, max_q_len: int = 0, pair_weight: int = 0,
+                   static_splits: int = 0, max_q_len: int = 0, min_q_len: int = 0, pair_weight: int = 0,
                    fused_combine: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Run the library on torch tensors; returns (out, lse, workspace).
 
@@ -269,7 +270,8 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                          window_expand_to_chunk=window_expand_to_chunk, landmark_chunk=landmark_chunk,
                          block_mask_tile=block_mask_tile, num_workers=num_workers,
                          split_min_units=split_min_units, force_split_units=force_split_units,
-                         max_partial_slots=max_partial_slots, max_q_len=max_q_len, pair_weight=pair_weight,
+                         max_partial_slots=max_partial_slots, max_q_len=max_q_len, min_q_len=min_q_len,
+                         pair_weight=pair_weight,
                          fused_combine=fused_combine)
     if split == "auto":
         params.split_mode, params.static_splits = paged_attn_plan_split(params, seq_lens, query_start_loc,
@@ -325,7 +327,7 @@ def run_batch(batch, *, out=None, lse=None, workspace=None, **kw):
         out = full_o[0].permute(1, 0, 2)
         lse = full_l[0].permute(1, 0)
     args = dict(softmax_scale=batch.softmax_scale, kv_layout=batch.kv_layout, causal=batch.causal,
-                max_q_len=batch.max_q_len,
+                max_q_len=batch.max_q_len, min_q_len=batch.min_q_len,
                 window=batch.window, window_expand_to_chunk=batch.window_expand_to_chunk,
                 landmark_chunk=batch.landmark_chunk, block_mask_tile=batch.block_mask_tile)
     args.update(kw)

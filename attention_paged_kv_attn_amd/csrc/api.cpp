@@ -14,7 +14,7 @@
 
 namespace pa {
 hipError_t launch_assign(const KParams& p, hipStream_t stream);
-hipError_t launch_attention(const KParams& p, int kind, int grid, bool small_only, hipStream_t stream);
+hipError_t launch_attention(const KParams& p, int kind, int grid, int paths, hipStream_t stream);
 hipError_t launch_combine(const KParams& p, bool out_f32, int grid, hipStream_t stream);
 hipError_t launch_static_begin(const KParams& p, hipStream_t stream);
 }  // namespace pa
@@ -77,7 +77,8 @@ pa_status check_params(const pa_params* p) {
   if (p->flags != 0) return PA_ERR_INVALID_ARG;
   if (p->split_mode != PA_SPLIT_DYNAMIC && p->split_mode != PA_SPLIT_STATIC) return PA_ERR_INVALID_ARG;
   if (p->static_splits < 0 || (p->split_mode == PA_SPLIT_STATIC && p->static_splits < 1)) return PA_ERR_INVALID_ARG;
-  if (p->max_q_len < 0) return PA_ERR_INVALID_ARG;
+  if (p->max_q_len < 0 || p->min_q_len < 0) return PA_ERR_INVALID_ARG;
+  if (p->max_q_len > 0 && p->min_q_len > p->max_q_len) return PA_ERR_INVALID_ARG;
   if (p->pair_weight < 0 || p->pair_weight > 99) return PA_ERR_INVALID_ARG;
   if (p->fused_combine != 0 && p->fused_combine != 1) return PA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
@@ -376,8 +377,11 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   kp.n_qb_max = L.n_qb_max;
   kp.static_S = is_static ? P.static_splits : 0;
   kp.max_q_len = P.max_q_len;
-  // the kernel choice is needed before the launch; made here for both
+  kp.min_q_len = P.min_q_len;
+  // the kernel build: without the prefill path when every Q-block is known to
+  // be small, without the decode path when every one is known to be large
   const bool small_only = is_static || (P.max_q_len > 0 && int64_t(P.max_q_len) * kp.G <= pa::kSmallMaxRows);
+  const bool large_only = !small_only && int64_t(P.min_q_len) * kp.G > pa::kSmallMaxRows;
   kp.pair_w = P.pair_weight ? P.pair_weight : (small_only ? PA_PAIR_WEIGHT_SMALL : PA_PAIR_WEIGHT_GENERAL);
   kp.fused = P.fused_combine ? 1 : 0;
   char* ws = static_cast<char*>(workspace);
@@ -414,8 +418,7 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   if (timing) (void)hipEventRecord(tc.ev[1], stream);
   const int64_t n_items = n_static_qb * P.static_splits;
   const int grid = is_static ? static_cast<int>(std::min<int64_t>(n_items, L.num_workers)) : L.num_workers;
-  // the small-Q-block kernel when every Q-block is known to be small
-  e = pa::launch_attention(kp, kind, grid, small_only, stream);
+  e = pa::launch_attention(kp, kind, grid, small_only ? 1 : large_only ? 2 : 0, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (timing) (void)hipEventRecord(tc.ev[2], stream);
   if (!P.fused_combine && (!is_static || P.static_splits > 1)) {

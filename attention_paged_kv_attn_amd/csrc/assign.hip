@@ -67,7 +67,8 @@ __device__ int assign_sequences(const KParams& p, int* sh, int* err, int* base_l
     const int a = p.qsl[b], c = p.qsl[b + 1];
     if ((b == 0 && a != 0) || c < a || (b == p.B - 1 && c != p.total_q)) atomicMax(err, (int)E_QSL);
     else if (c - a > p.seq_lens[b]) atomicMax(err, (int)E_QLEN);
-    else if (p.max_q_len > 0 && c - a > p.max_q_len) atomicMax(err, (int)E_QLEN_HINT);
+    else if ((p.max_q_len > 0 && c - a > p.max_q_len) || (c > a && c - a < p.min_q_len))
+      atomicMax(err, (int)E_QLEN_HINT);
   }
   __syncthreads();
   if (*err != E_NONE) {

@@ -2041,14 +2041,21 @@ __device__ __forceinline__ void static_items(uint64_t pk) {
 // the persistent kernel
 // ---------------------------------------------------------------------------
 
-// SMALL: the kernel for batches whose Q-blocks are all small (decode and
-// MTP, and every static split).  It is the same code without the large-Q-block
-// path, compiled on its own: sharing a kernel with the large path's register
-// demand slows the decode loops (measured 7-13%), although their instruction
-// streams come out nearly the same.  A large Q-block reaching it is reported
-// (E_QLEN_HINT) and skipped.
-template <int KIND, int D, bool FAST, bool SMALL>
+// PATHS: which Q-block paths the kernel is built with.  kPathsSmall is the
+// kernel for batches whose Q-blocks are all small (decode and MTP, and every
+// static split); kPathsLarge the one for batches whose Q-blocks are all large
+// (prefill chunks, the sliding-window forward).  Each is the same code with
+// the other path left out, compiled on its own: sharing one kernel with the
+// other path's register demand costs the decode loops 7-13% and the prefill
+// loops 2-8% (measured), although their instruction streams come out nearly
+// the same.  The small-only kernel reports a large Q-block (E_QLEN_HINT) and
+// skips it; the large-only kernel runs the few-row tail Q-blocks of long
+// sequences on the 128-row path (Assign rejects short sequences under it).
+constexpr int kPathsAll = 0, kPathsSmall = 1, kPathsLarge = 2;
+
+template <int KIND, int D, bool FAST, int PATHS>
 __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention_kernel(KParams) {
+  constexpr bool SMALL = PATHS == kPathsSmall, LARGE = PATHS == kPathsLarge;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t pk = kparams_addr();
   const KParams& p = kparams_at(pk);
@@ -2099,7 +2106,9 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
       if (nq == 0) { ++q; continue; }
       const int u0 = a - S, u1 = min(b_end, S + nq) - S;
       const QBlock x = load_qblock(p, q);
-      if (x.rows <= kSmallMaxRows && p.bm == nullptr) {
+      // (the large-only kernel runs every Q-block, the last few tokens of a
+      // long sequence included, on the 128-row path)
+      if (!LARGE && x.rows <= kSmallMaxRows && p.bm == nullptr) {
         // the maximal run of small Q-blocks from here, inside this worker's range
         int run_end = S + u1, qq = q + 1;
         while (run_end < b_end && qq < n_qb) {
@@ -2118,7 +2127,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
       qblock_tiles(p, x.ctx, x.pos_lo, x.pos_hi, t_lo, t_hi);
       const bool final_out = p.n_splits[q] == 1;
       const int slot = final_out ? 0 : p.slot_base[q] + (vw - wm.worker_of(S));
-      if (x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
+      if (!LARGE && x.rows <= kSmallMaxRows) small_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot);
       else if constexpr (SMALL) {
         if (threadIdx.x == 0) p.hdr[H_ERROR] = E_QLEN_HINT;
         a = S + u1;
@@ -2134,39 +2143,40 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   }
 }
 
-template <int KIND, int D, bool FAST, bool SMALL>
+template <int KIND, int D, bool FAST, int PATHS>
 static hipError_t launch_attention_t(const KParams& p, int grid, hipStream_t stream) {
   const int lds = Lds<KIND, D, FAST>::DYN;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST, SMALL>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST, PATHS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL((attention_kernel<KIND, D, FAST, SMALL>), dim3(grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((attention_kernel<KIND, D, FAST, PATHS>), dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-template <int KIND, int D, bool SMALL>
+template <int KIND, int D, int PATHS>
 static hipError_t launch_attention_kd(const KParams& p, int grid, hipStream_t stream) {
-  return p.page_size >= kUnitKeys ? launch_attention_t<KIND, D, true, SMALL>(p, grid, stream)
-                                  : launch_attention_t<KIND, D, false, SMALL>(p, grid, stream);
+  return p.page_size >= kUnitKeys ? launch_attention_t<KIND, D, true, PATHS>(p, grid, stream)
+                                  : launch_attention_t<KIND, D, false, PATHS>(p, grid, stream);
 }
 
-template <bool SMALL>
+template <int PATHS>
 static hipError_t launch_attention_s(const KParams& p, int kind, int grid, hipStream_t stream) {
-  if (kind == KIND_F32) return p.D == 64 ? launch_attention_kd<KIND_F32, 64, SMALL>(p, grid, stream)
-                                         : launch_attention_kd<KIND_F32, 128, SMALL>(p, grid, stream);
-  if (kind == KIND_BF16) return p.D == 64 ? launch_attention_kd<KIND_BF16, 64, SMALL>(p, grid, stream)
-                                          : launch_attention_kd<KIND_BF16, 128, SMALL>(p, grid, stream);
-  return p.D == 64 ? launch_attention_kd<KIND_F8, 64, SMALL>(p, grid, stream)
-                   : launch_attention_kd<KIND_F8, 128, SMALL>(p, grid, stream);
+  if (kind == KIND_F32) return p.D == 64 ? launch_attention_kd<KIND_F32, 64, PATHS>(p, grid, stream)
+                                         : launch_attention_kd<KIND_F32, 128, PATHS>(p, grid, stream);
+  if (kind == KIND_BF16) return p.D == 64 ? launch_attention_kd<KIND_BF16, 64, PATHS>(p, grid, stream)
+                                          : launch_attention_kd<KIND_BF16, 128, PATHS>(p, grid, stream);
+  return p.D == 64 ? launch_attention_kd<KIND_F8, 64, PATHS>(p, grid, stream)
+                   : launch_attention_kd<KIND_F8, 128, PATHS>(p, grid, stream);
 }
 
-hipError_t launch_attention(const KParams& p, int kind, int grid, bool small_only, hipStream_t stream) {
-  return small_only ? launch_attention_s<true>(p, kind, grid, stream)
-                    : launch_attention_s<false>(p, kind, grid, stream);
+hipError_t launch_attention(const KParams& p, int kind, int grid, int paths, hipStream_t stream) {
+  if (paths == kPathsSmall) return launch_attention_s<kPathsSmall>(p, kind, grid, stream);
+  if (paths == kPathsLarge) return launch_attention_s<kPathsLarge>(p, kind, grid, stream);
+  return launch_attention_s<kPathsAll>(p, kind, grid, stream);
 }
 
 }  // namespace pa

@@ -55,6 +55,7 @@ struct KParams {
   int32_t P, L_min, force_L, max_slots, n_qb_max;
   int32_t static_S;  // > 0: static split, every Q-block cut into static_S equal tile ranges (no task map)
   int32_t max_q_len; // > 0: the caller's bound on every q_len (checked by Assign)
+  int32_t min_q_len; // > 0: the caller's bound below every non-zero q_len (checked by Assign)
   int32_t pair_w;    // percent of a worker pair's 2L units given to its first worker
   int32_t fused;     // 1: the last workgroup to finish a split Q-block merges it (no Combine launch)
   // workspace

@@ -64,6 +64,7 @@ class PagedBatch:
     dense_v: Optional[list] = None
     info: dict = field(default_factory=dict)
     max_q_len: int = 0            # the largest q_len of the batch (0 = not stated)
+    min_q_len: int = 0            # the smallest non-zero q_len of the batch (0 = not stated)
 
     @property
     def num_seqs(self) -> int:
@@ -256,7 +257,8 @@ def build_batch(rng: np.random.Generator, *, name: str, kind: str, Hq: int, Hkv:
                       causal=causal, window=window, window_expand_to_chunk=window_expand_to_chunk,
                       landmark_chunk=landmark_chunk, block_mask=block_mask, block_mask_tile=block_mask_tile,
                       scales=scales, out_heads_major=out_heads_major, dense_k=dense_k, dense_v=dense_v,
-                      info=info, max_q_len=max(q_len) if q_len else 0)
+                      info=info, max_q_len=max(q_len) if q_len else 0,
+                      min_q_len=min((x for x in q_len if x > 0), default=0))
 
 
 # ---------------------------------------------------------------------------
@@ -343,7 +345,7 @@ def replay_variants(n: int = 4, batch: int = 16, total_q: int = 32, max_q_len: i
         kw = dict(base.__dict__)
         kw.update(name=f"replay_v{v}", block_table=torch.from_numpy(bt),
                   seq_lens=torch.from_numpy(ctx.astype(np.int32)), query_start_loc=torch.from_numpy(qsl),
-                  max_q_len=max_q_len)
+                  max_q_len=max_q_len, min_q_len=0)
         out.append(PagedBatch(**kw))
     return out
 

@@ -130,6 +130,12 @@ typedef struct pa_params {
                                    prefill path runs (faster decode).  A sequence longer than
                                    the bound is device error PA_DEV_QLEN_HINT (outputs then
                                    unspecified). */
+  int32_t min_q_len;            /* 0, or a bound below every non-zero q_len (a scheduler's
+                                   prefill chunk size).  When min_q_len * Hq / Hkv > 16 every
+                                   Q-block is large and a kernel built without the decode path
+                                   runs (faster prefill).  A shorter non-empty sequence is
+                                   device error PA_DEV_QLEN_HINT.  Must not exceed max_q_len
+                                   when both are set. */
   int32_t pair_weight;          /* 1..99: percent of each worker pair's 2L units given to its
                                    first worker (the workgroup dispatched first onto a compute
                                    unit, which the hardware favours); 50 is the even split.
@@ -201,7 +207,7 @@ typedef enum pa_device_error {
   PA_DEV_SLOTS = 3,          /* more split partials than max_partial_slots */
   PA_DEV_BAD_PAGE = 5,       /* a block_table entry needed for a key is outside [0, num_pages) */
   PA_DEV_STATIC_ROWS = 6,    /* PA_SPLIT_STATIC with a sequence of q_len * Hq / Hkv > 16 */
-  PA_DEV_QLEN_HINT = 7       /* a sequence's q_len exceeds params->max_q_len */
+  PA_DEV_QLEN_HINT = 7       /* a q_len above params->max_q_len, or non-zero below min_q_len */
 } pa_device_error;
 
 /*

@@ -470,9 +470,29 @@ def test_decode_kernel_choice_by_q_len_bound():
     rng = np.random.default_rng(3)
     b = W.build_batch(rng, name="hint_prefill", kind="bf16", Hq=8, Hkv=2, d=64, page_size=64,
                       ctx=[300, 200], q_len=[100, 1], num_pages=10)
-    g, out4, lse4, ws4 = gpu_run(b, max_q_len=1)
+    g, out4, lse4, ws4 = gpu_run(b, max_q_len=1, min_q_len=0)
     h, _ = header(ws4, params_of(g))
     assert h[7] == 7
+    # ... and a lower bound above a sequence's q_len
+    g, out5, lse5, ws5 = gpu_run(b, max_q_len=0, min_q_len=100)
+    h, _ = header(ws5, params_of(g))
+    assert h[7] == 7
+
+
+@pytest.mark.parametrize("kind", ["bf16", "e4m3"])
+def test_prefill_kernel_choice_by_q_len_bound(kind):
+    """Prefill batches run the large-Q-block kernel when the caller states
+    min_q_len (run_batch passes the batch's own); the general kernel agrees."""
+    rng = np.random.default_rng(12)
+    b = W.build_batch(rng, name=f"prefill_bound_{kind}", kind=kind, Hq=32, Hkv=8, d=128, page_size=64,
+                      ctx=[900, 1500, 700], q_len=[900, 400, 0], quant_mode="tensor" if kind == "e4m3" else None)
+    assert b.min_q_len == 400
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    g, out2, lse2, ws2 = gpu_run(b, min_q_len=0, max_q_len=0)
+    check_no_device_error(ws2, g)
+    compare(b, out2, lse2)
 
 
 @pytest.mark.parametrize("make,kw", [
