@@ -564,6 +564,27 @@ def test_graph_replay_with_changing_batch(split):
                 compare(v, o_r, l_r)
 
 
+def test_small_kernel_with_block_mask_and_f32_static():
+    """Decode rows under a block mask (small Q-blocks on the masked segment
+    path of the small-Q-block kernel), and fp32 decode under a static split
+    and the fused merge (fp32 outputs)."""
+    rng = np.random.default_rng(31)
+    b = W.build_batch(rng, name="decode_mask", kind="bf16", Hq=32, Hkv=8, d=128, page_size=64,
+                      ctx=[3000, 700, 1800, 129], q_len=[1, 2, 4, 1], block_mask_skip=0.5)
+    assert b.max_q_len * 4 <= 16
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    rng = np.random.default_rng(32)
+    b = W.build_batch(rng, name="decode_f32", kind="f32", Hq=4, Hkv=1, d=64, page_size=16,
+                      ctx=[37, 300, 1000, 64], q_len=[1, 4, 2, 0], num_pages=120)
+    for kw in ({"split": "static", "static_splits": 3}, {"split": "static", "static_splits": 3, "fused_combine": True},
+               {"force_split_units": 2, "max_partial_slots": 512, "fused_combine": True}):
+        g, out, lse, ws = gpu_run(b, **kw)
+        check_no_device_error(ws, g)
+        compare(b, out, lse)
+
+
 def test_auto_policy_runs_each_shape():
     for b in (W.splitk_decode(q_len=1, batch=12, ctx_lo=100, ctx_hi=6000),
               W.build_batch(np.random.default_rng(5), name="uniform", kind="bf16", Hq=32, Hkv=8, d=128,
