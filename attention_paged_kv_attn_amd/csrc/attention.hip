@@ -1112,14 +1112,12 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
 // pipeline and synchronise the workgroup at each of the many short decode
 // Q-blocks of a ragged batch.
 // ---------------------------------------------------------------------------
-#ifndef PA_HALF_STEP
-#define PA_HALF_STEP 2
-#endif
-// decode streaming with loads half a tile ahead (bit 0: bf16, bit 1: fp8).
-// fp8 only: a bf16 tile is twice the registers, and holding the next K
-// through the PV spills (measured slower); for fp8 it is ~4% faster
+// decode streaming with loads half a tile ahead: fp8 only.  A bf16 tile is
+// twice the registers, and holding the next K through the PV spills
+// (measured slower); for fp8 it is ~4% faster.  (Two whole fp8 tiles in
+// registers spill as well.)
 template <int KIND>
-constexpr bool kHalfStep = (KIND == KIND_BF16 && (PA_HALF_STEP & 1)) || (KIND == KIND_F8 && (PA_HALF_STEP & 2));
+constexpr bool kHalfStep = KIND == KIND_F8;
 
 template <int KIND, int D, bool FAST>
 struct StreamRec {
