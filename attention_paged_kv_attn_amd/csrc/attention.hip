@@ -1456,7 +1456,9 @@ struct Stage {
   // global -> registers for the given tile.  Thread t stages K chunks
   // c = i * 256 + t (lane c % 64 of operand (mb, ks) = c / 64, a row of the
   // tile: key 16 mb + lane % 16) and V rows 32 ks2 + 16 half + 4 (lane / 16) + j.
-  // FAST: `page` is the tile's physical page, from the caller's page window
+  // FAST: `page` is the tile's physical page, from the caller's page window.
+  // WITH_K = false: V only (K goes straight to LDS)
+  template <bool WITH_K = true>
   __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, int page) {
     Tile<C::ELT, FAST> t;
     // the tile's scales travel with its data, so the step that uses them
@@ -1472,7 +1474,7 @@ struct Stage {
     const int ln = tid & 63, m = ln & 15, hh = ln >> 4;
     const bool full = t.nvalid == kUnitKeys;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < (WITH_K ? KCH : 0); ++i) {
       const int mk = (i * kThreads + tid) >> 6;            // uniform per wave
       int mb, col;                                          // col: byte offset in the row
       if constexpr (KIND == KIND_F32) {
@@ -1524,10 +1526,11 @@ struct Stage {
   }
 
   // registers -> LDS buffer
+  template <bool WITH_K = true>
   __device__ __forceinline__ void store(char* kbuf, char* vbuf) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < (WITH_K ? KCH : 0); ++i) {
       const int c = i * kThreads + tid;
       *reinterpret_cast<KReg*>(kbuf + c * sizeof(KReg)) = kr[i];
     }
@@ -1582,6 +1585,7 @@ struct DirectStage {
   uint32_t k_col, v_col;      // byte column within a row
   int k_row0, v_row0;         // row of load i = 0 (K: + 16 i, V: + 16 i)
   uint32_t k_lane, v_lane;    // byte offsets of the lane's rows for load i = 0
+  uint32_t k8_lane;           // fp8 K (see issue_k8): row m, byte 16 hh of a 64-byte chunk
 
   // (re)point at sequence s.b, kv head s.g; the page window survives while the
   // sequence stays the same
@@ -1613,6 +1617,7 @@ struct DirectStage {
     v_col = 16u * (sl ^ (2 * (v_row0 & 7)));             // swizzled 16-byte column (row & 7 is i-invariant)
     k_lane = (uint32_t)k_row0 * kss + k_col;
     v_lane = (uint32_t)v_row0 * vss + v_col;
+    k8_lane = (uint32_t)m * kss + 16u * hh;
   }
 
   __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
@@ -1657,6 +1662,14 @@ struct DirectStage {
   // memory: they are read as they are (their scores are masked by select)
   // and their V rows are zeroed once landed (zero_tail), so no garbage reaches
   // P V.  Row 16 i of a load moves the scalar base only.
+  // fp8, d = 128: the K tile straight to LDS in the operand order of the
+  // 16x16x128 MFMA with each lane's 32 bytes taken as two 16-byte chunks:
+  // chunk c of operand mb (rows 16 mb + m, bytes 64 c + 16 hh) lands
+  // lane-linearly at kbuf + 1 KiB (2 mb + c).  Wave w loads operand mb = w.
+  __device__ __forceinline__ void issue_k8(int c, char* kbuf) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    gload16_lds(wave_uniform(pk_b + (uint32_t)(16 * wave) * kss + 64u * c), kbuf + 1024 * (2 * wave + c), k8_lane, 0u);
+  }
   __device__ __forceinline__ void issue(int i, char* kbuf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (i < 4) gload16_lds(wave_uniform(pk_b + (uint32_t)(16 * i) * kss), kbuf + 1024 * (4 * i + wave), k_lane, 0u);
@@ -1708,6 +1721,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   constexpr int MD = C::MD;
   constexpr int NB = 2;
   constexpr bool DIRECT = KIND == KIND_BF16 && D == 128 && FAST;
+  // fp8, d = 128, one page per tile: K straight to LDS (issue_k8), V staged
+  // through registers (widened to bf16 there); Q then takes K's chunk order
+  constexpr bool DKF8 = KIND == KIND_F8 && D == 128 && FAST;
   // Row sums of P stay on the VALU in fp32: an MFMA sum of the bf16 P operand
   // carries its rounding (up to 2^-9 on the largest term, which under the lazy
   // rescale is no longer exactly 1) straight into the LSE.
@@ -1739,8 +1755,19 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     rok[nb] = r < x.rows;
     rowi[nb] = rok[nb] ? r : 0;
     const int tok = x.q0 + x.t0 + rowi[nb] / p.G, head = x.g * p.G + rowi[nb] % p.G;
-    load_qk_row<KIND, D>(rok[nb] ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
-                                 : nullptr, h, qB[nb]);
+    const char* qrow = rok[nb] ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
+                               : nullptr;
+    if constexpr (DKF8) {
+      // bytes 16 h .. 16 h + 15 and 64 + 16 h .. 79 + 16 h of the row, as issue_k8 lays K out
+      const u32x4 c0 = qrow ? *reinterpret_cast<const u32x4*>(qrow + 16 * h) : u32x4{0, 0, 0, 0};
+      const u32x4 c1 = qrow ? *reinterpret_cast<const u32x4*>(qrow + 64 + 16 * h) : u32x4{0, 0, 0, 0};
+      qB[nb][0] = __builtin_bit_cast(long, u32x2{c0[0], c0[1]});
+      qB[nb][1] = __builtin_bit_cast(long, u32x2{c0[2], c0[3]});
+      qB[nb][2] = __builtin_bit_cast(long, u32x2{c1[0], c1[1]});
+      qB[nb][3] = __builtin_bit_cast(long, u32x2{c1[2], c1[3]});
+    } else {
+      load_qk_row<KIND, D>(qrow, h, qB[nb]);
+    }
     rm[nb].pos = x.ctx - x.ql + x.t0 + rowi[nb] / p.G;
     rm[nb].left = p.window > 0 ? window_left(p, rm[nb].pos) : 0;
     rm[nb].bit = true;
@@ -1773,6 +1800,15 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       ds.load(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
       ds.zero_tail(vstage<true>(0));
+    } else if constexpr (DKF8) {
+      ds.prep(p, s, tile_of(c0));
+      ds.issue_k8(0, smem);
+      ds.issue_k8(1, smem);
+      stg.template load<false>(p, s, tile_of(c0), ds.page_of_tile(p, tile_of(c0) * kUnitKeys));
+      stg.template store<false>(smem, smem + C::K_TILE);
+      wait_vmem();
+      cur_ksc = stg.ksc;
+      cur_vsc = stg.vsc;
     } else {
       stg.load(p, s, tile_of(c0), FAST ? ds.page_of_tile(p, tile_of(c0) * kUnitKeys) : -1);
       stg.store(smem, smem + C::K_TILE);
@@ -1788,6 +1824,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       char* vbuf = kbuf + C::K_TILE;
       const bool more = u + 1 < c0 + cn;
       char* nkb = smem + (buf ^ 1) * C::K_TILE;
+      char* nkb_stage = smem + (buf ^ 1) * C::STAGE;
       char* nvb = nullptr;
       if constexpr (DIRECT) {
         // the next tile's DMAs go out between the QK MFMAs below (the last
@@ -1799,7 +1836,15 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           for (int i = 0; i < 8; ++i) ds.issue(i, nkb, nvb);
         }
       } else if (more) {
-        stg.load(p, s, tile_of(u + 1), FAST ? ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys) : -1);
+        if constexpr (DKF8) {
+          // (issued here rather than spread over the QK MFMAs: measured faster)
+          ds.prep(p, s, tile_of(u + 1));
+          ds.issue_k8(0, nkb_stage);
+          ds.issue_k8(1, nkb_stage);
+          stg.template load<false>(p, s, tile_of(u + 1), ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys));
+        } else {
+          stg.load(p, s, tile_of(u + 1), FAST ? ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys) : -1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       const int tile = tile_of(u);
@@ -1847,9 +1892,15 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) qc[nb] = cat4(qB[nb][0], qB[nb][1], qB[nb][2], qB[nb][3]);
           auto kread4 = [&](int mb) -> i32x8 {
-            const char* at = kbuf + (mb * 4 * 64 + lane) * 8;
-            return cat4(*reinterpret_cast<const long*>(at), *reinterpret_cast<const long*>(at + 512),
-                        *reinterpret_cast<const long*>(at + 1024), *reinterpret_cast<const long*>(at + 1536));
+            if constexpr (DKF8) {
+              const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + 1024 * (2 * mb) + 16 * lane);
+              const u32x4 b = *reinterpret_cast<const u32x4*>(kbuf + 1024 * (2 * mb + 1) + 16 * lane);
+              return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+            } else {
+              const char* at = kbuf + (mb * 4 * 64 + lane) * 8;
+              return cat4(*reinterpret_cast<const long*>(at), *reinterpret_cast<const long*>(at + 512),
+                          *reinterpret_cast<const long*>(at + 1024), *reinterpret_cast<const long*>(at + 1536));
+            }
           };
           i32x8 kc = kread4(0);
 #pragma unroll
@@ -1977,7 +2028,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         ds.zero_tail(nvb);
       } else if (more) {
         char* nk = smem + (buf ^ 1) * C::STAGE;
-        stg.store(nk, nk + C::K_TILE);
+        stg.template store<!DKF8>(nk, nk + C::K_TILE);
+        if constexpr (DKF8) wait_vmem();                 // this wave's K DMAs have landed
         cur_ksc = stg.ksc;
         cur_vsc = stg.vsc;
       }
