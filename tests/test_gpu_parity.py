@@ -585,6 +585,18 @@ def test_small_kernel_with_block_mask_and_f32_static():
         compare(b, out, lse)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_small_pages(d):
+    """FP8 with 16-token pages (tiles span four pages: the register-staged
+    prefill path and per-key page lookups), prefill rows and decode rows."""
+    rng = np.random.default_rng(41 + d)
+    b = W.build_batch(rng, name=f"fp8_pages16_d{d}", kind="e4m3", Hq=8, Hkv=2, d=d, page_size=16,
+                      ctx=[700, 300, 90], q_len=[300, 1, 4], quant_mode="tensor", q_quant="token_head")
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
 def test_auto_policy_runs_each_shape():
     for b in (W.splitk_decode(q_len=1, batch=12, ctx_lo=100, ctx_hi=6000),
               W.build_batch(np.random.default_rng(5), name="uniform", kind="bf16", Hq=32, Hkv=8, d=128,
