@@ -673,3 +673,36 @@ def test_edge_cases():
     b = W.splitk_decode(q_len=3, batch=4, ctx_lo=70, ctx_hi=500)
     g, out, lse, ws = gpu_run(b, causal=False)
     compare(b, out, lse, causal=False)
+
+
+@pytest.mark.parametrize("make", [
+    lambda: W.splitk_decode(q_len=[1, 2, 4, 3] * 3, batch=12, ctx_lo=64, ctx_hi=3000),
+    lambda: W.hybrid_chunked(batch=6, chunk=200, history=700, dec_lo=100, dec_hi=2000),
+], ids=["mtp_mix", "hybrid"])
+def test_strided_views_bitwise(make):
+    """Q as the head slice of a fused QKV buffer, the block table as the
+    leading columns of a wider table, O as a slice of wider rows and LSE with
+    a column stride of 2: the same bits as with contiguous tensors, and the
+    padding between the views' elements left untouched."""
+    import dataclasses
+    b = make()
+    g, o1, l1, _ = gpu_run(b)
+    T, Hq, d = g.q.shape
+    Hkv, mp = g.num_kv_heads, g.block_table.shape[1]
+    qkv = torch.zeros((T, Hq + 2 * Hkv, d), dtype=g.q.dtype, device=DEV)
+    qkv[:, :Hq] = g.q
+    bt = torch.full((g.num_seqs, mp + 37), -1, dtype=torch.int32, device=DEV)
+    bt[:, :mp] = g.block_table
+    gs = dataclasses.replace(g, q=qkv[:, :Hq], block_table=bt[:, :mp])
+    ob = torch.full((T, Hq, d + 64), 7.0, dtype=o1.dtype, device=DEV)
+    lb = torch.full((T, 2 * Hq + 3), 7.0, dtype=torch.float32, device=DEV)
+    o2, l2 = ob[:, :, :d], lb[:, 1:1 + 2 * Hq:2]
+    say(f"  launch {b.name} strided q {tuple(gs.q.stride())} bt {tuple(gs.block_table.stride())} "
+        f"out {tuple(o2.stride())} lse {tuple(l2.stride())}")
+    B.run_batch(gs, out=o2, lse=l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.contiguous().view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.contiguous().view(torch.int32))
+    assert (ob[:, :, d:] == 7.0).all()
+    assert (lb[:, 0] == 7.0).all() and (lb[:, 2:2 * Hq + 1:2] == 7.0).all() and (lb[:, 2 * Hq + 1:] == 7.0).all()
+    compare(b, o2, l2)
