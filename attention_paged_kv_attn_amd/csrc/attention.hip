@@ -237,9 +237,15 @@ __device__ __forceinline__ float held(float v) { return __int_as_float(held(__fl
 // Loads at base + soff + voff: `base + soff` is wave-uniform (scalar), voff a
 // 32-bit per-lane offset, so the address is a scalar base plus a VGPR offset
 // when the compiler keeps the base in scalar registers.
+//
+// The 16-byte load is non-temporal: its users stream K/V rows that are read
+// once (decode tiles), and not allocating them in the caches moved the bf16
+// decode kernel from 5.05 to 5.35 TB/s (NHD) and 5.31 to 5.95 TB/s (HND) on
+// MI355X.  The 8-byte load (the fp8 decode rows) stays temporal: made
+// non-temporal it slowed fp8 decode by 41%.
 #define PA_GLOBAL __attribute__((address_space(1)))
 __device__ __forceinline__ u32x4 gload16(const char* base, uint32_t voff, uint32_t soff) {
-  return *(const PA_GLOBAL u32x4*)(base + soff + voff);
+  return __builtin_nontemporal_load((const PA_GLOBAL u32x4*)(base + soff + voff));
 }
 __device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL u32x2*)(base + soff + voff);
