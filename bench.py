@@ -337,22 +337,31 @@ def summarize_profiles(d):
     steps, warmup = bench_line["steps"], bench_line["warmup"]
     n_dec = 1 + warmup + steps                       # run_batch once, warmup, timed steps
     legs = {bench_line["config"]["workload"]: att[:n_dec]}
+    off = n_dec
+    events = {bench_line["config"]["workload"]: bench_line["kernels_ms"]["attention"]}
+    n_leg = 1 + warmup + max(5, steps // 2)
     if "prefill" in bench_line:
-        n_pre = 1 + warmup + max(5, steps // 2)
-        legs[bench_line["prefill"]["workload"]] = att[n_dec:n_dec + n_pre]
+        legs[bench_line["prefill"]["workload"]] = att[off:off + n_leg]
+        events[bench_line["prefill"]["workload"]] = bench_line["prefill"]["kernels_ms"]["attention"]
+        off += n_leg
+    for a in bench_line.get("also", []):
+        if "kernels_ms" not in a:                     # a graph replay: launches of its own shape; stop here
+            break
+        legs[a["workload"]] = att[off:off + n_leg]
+        events[a["workload"]] = a["kernels_ms"]["attention"]
+        off += n_leg
     with open(os.path.join(out_dir, "bench_default_kernel_stats.md"), "w") as f:
         f.write("# rocprofv3 kernel statistics of the default bench command\n\n")
         f.write("| kernel | calls | average ns | min ns | max ns | % |\n|---|---|---|---|---|---|\n")
         for r in stats:
             f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                     f"{r['MaxNs']} | {r['Percentage']} |\n")
-        f.write("\nThe attention kernel serves both legs under one name; the per-dispatch trace splits them "
+        f.write("\nThe attention kernel serves every leg under one name; the per-dispatch trace splits them "
                 "in launch order (first call, warmup, timed steps of each leg):\n\n")
         f.write("| leg | dispatches | average ns (timed steps) | bench HIP-event ms |\n|---|---|---|---|\n")
         for wl, ds in legs.items():
             timed = [x[1] for x in ds[-(steps if wl == bench_line['config']['workload'] else max(5, steps // 2)):]]
-            ev = bench_line["kernels_ms"]["attention"] if wl == bench_line["config"]["workload"] \
-                else bench_line["prefill"]["kernels_ms"]["attention"]
+            ev = events[wl]
             f.write(f"| {wl} | {len(ds)} | {np.mean(timed):.0f} | {ev} |\n")
         f.write("\nCommands:\n\n```\n" + cmds + "\n```\n")
     # per-workload counter summaries
@@ -414,7 +423,8 @@ def main():
     ap.add_argument("--workload", default="splitk_decode_q1_NHD", choices=sorted(WORKLOADS))
     ap.add_argument("--prefill-workload", default="prefill_bf16_dense", choices=sorted(WORKLOADS) + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", default="", help="comma-separated extra workloads to time (reported under 'also')")
+    ap.add_argument("--extra", default="splitk_decode_q1_HND,splitk_decode_fp8_q1_NHD",
+                    help="comma-separated extra workloads to time (reported under 'also'); '' for none")
     ap.add_argument("--profile-leg", default=None, choices=sorted(WORKLOADS),
                     help="time only this workload (for rocprofv3 counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
