@@ -325,3 +325,34 @@ def test_expand_to_chunk_changes_only_unaligned_rows():
     same = (pos - W_ + 1 <= 0) | ((pos - W_ + 1) % C == 0)
     assert np.array_equal(Oe[same], On[same]) and np.array_equal(Le[same], Ln[same])
     assert np.all(np.abs(Le[~same] - Ln[~same]).max(axis=1) > 0)
+
+
+def _empty_row_batch():
+    """A chunk where every other row sees no key although the key span of its
+    row block is non-empty: window 1 (no expansion) leaves each query only its
+    own key, and landmark chunk 2 hides the keys j with (j + 1) even, so a
+    query at an odd position sees nothing."""
+    rng = np.random.default_rng(47)
+    return W.build_batch(rng, name="empty_rows", kind="f32", Hq=4, Hkv=2, d=16, page_size=16,
+                         ctx=[23, 9], q_len=[13, 9], keep_dense=True, window=1,
+                         window_expand_to_chunk=False, landmark_chunk=2)
+
+
+def test_rows_without_visible_keys_inside_a_nonempty_span():
+    b = _empty_row_batch()
+    O, L = run_oracle(b)
+    Ob, Lb = _brute(b)
+    qsl, ctx = b.query_start_loc.tolist(), b.seq_lens.tolist()
+    empty = np.zeros(b.total_q, dtype=bool)
+    for s in range(b.num_seqs):
+        for t in range(qsl[s], qsl[s + 1]):
+            pos = ctx[s] - (qsl[s + 1] - qsl[s]) + (t - qsl[s])
+            empty[t] = pos % 2 == 1
+    assert empty.any() and (~empty).any()
+    # brute force and the definition: O = 0 and LSE = -inf exactly, no NaN
+    assert np.all(Ob[empty] == 0.0) and np.all(Lb[empty] == -math.inf)
+    assert not np.isnan(O).any() and not np.isnan(L).any()
+    assert np.all(O[empty] == 0.0) and np.all(L[empty] == -math.inf)
+    # the other rows see exactly one key: O = that value row, LSE = its score
+    assert np.abs(O[~empty] - Ob[~empty]).max() <= 1e-12
+    assert np.abs(L[~empty] - Lb[~empty]).max() <= 1e-12

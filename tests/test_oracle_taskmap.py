@@ -6,10 +6,19 @@ from attention_paged_kv_attn_amd import workloads as W
 from oracle import brute, taskmap
 
 
-def _check_invariants(tm):
+def _check_invariants(tm, split_min_units=8, force_split_units=0):
     U, L, P = tm["U"], tm["L"], tm["P"]
     prefix, n = tm["unit_prefix"], tm["n_units"]
     assert prefix[0] == 0 and prefix[-1] == U and np.all(np.diff(prefix) == n)
+    # the chunk length: forced, else the larger of the floor and the total load
+    # spread over the P workers, rounded up (U <= P L always holds then)
+    if force_split_units > 0:
+        assert L == force_split_units
+    else:
+        # the smallest L >= L_min with L P >= U: one unit fewer would leave
+        # units without a worker (unless L is already at the floor)
+        assert L >= split_min_units and L * P >= U
+        assert L == split_min_units or (L - 1) * P < U
     nw = tm["n_workers"]
     L0 = tm["L0"]
     assert 1 <= L0 <= 2 * L - 1
@@ -42,7 +51,14 @@ def _check_invariants(tm):
             run += tm["n_splits"][q]
         else:
             assert sb[q] == -1
+    # each worker's range cuts at most two Q-blocks (its first and its last)
     assert run == tm["n_slots"] <= 2 * max(nw, 1)
+    if force_split_units == 0:
+        # P workers suffice: pairs own 2L units each and U <= P L; only an odd P
+        # whose last pair is cut unevenly (L0 < L) needs the pair's second worker
+        assert nw <= P + (P % 2 if L0 < L else 0)
+        if P % 2 == 0 or L0 >= L:
+            assert tm["n_slots"] <= 2 * P
 
 
 @pytest.mark.parametrize("weight", [50, 60, 99, 1])
@@ -59,6 +75,18 @@ def test_pair_weight_split_invariants(weight):
     assert tm["L0"] == tm["L"]
     for w in range(tm["n_workers"]):
         assert taskmap.worker_range(w, tm["L"], tm["L0"], tm["U"]) == (w * tm["L"], min(tm["U"], (w + 1) * tm["L"]))
+
+
+@pytest.mark.parametrize("P,weight", [(7, 30), (9, 1), (5, 50), (8, 20)])
+def test_odd_worker_counts_and_uneven_pairs(P, weight):
+    """An odd P whose last pair is cut unevenly may use P + 1 workers; the slot
+    bound then holds against the workers actually used."""
+    rng = np.random.default_rng(11)
+    ctx = W.decode_ctx_lengths(rng, 40, 64, 3000)
+    for L_min in (1, 8, 400):
+        tm = taskmap.build(ctx, np.arange(41), Hq=16, Hkv=4, num_workers=P, pair_weight=weight,
+                           split_min_units=L_min)
+        _check_invariants(tm, split_min_units=L_min)
 
 
 @pytest.mark.parametrize("P", [1, 7, 64, 512])
@@ -82,7 +110,7 @@ def test_hybrid_and_forced_split():
     _check_invariants(tm)
     tm1 = taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=512, force_split_units=1)
     assert tm1["L"] == 1 and tm1["n_slots"] == sum(x for x in tm1["n_units"] if x >= 2)
-    _check_invariants(tm1)
+    _check_invariants(tm1, force_split_units=1)
 
 
 def _brute_units(desc, ctx, ql, **rule):
