@@ -54,7 +54,8 @@ class pa_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "header", "seq_qb_base", "qb_desc", "unit_prefix", "n_splits", "slot_base", "combine_list",
         "done", "partial_lse", "partial_o", "total")] + [
-        ("n_qb_max", ctypes.c_int32), ("max_slots", ctypes.c_int32), ("num_workers", ctypes.c_int32)]
+        ("n_qb_max", ctypes.c_int32), ("max_slots", ctypes.c_int32), ("num_workers", ctypes.c_int32),
+        ("slot_rows", ctypes.c_int32)]
 
 
 class pa_device_info(ctypes.Structure):
@@ -306,12 +307,11 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     qt, kt, vt = as_pa_tensor(q), kv_logical(k_cache, kv_layout), kv_logical(v_cache, kv_layout)
     ot, lt = as_pa_tensor(out), as_pa_tensor(lse)
     mt = as_pa_tensor(block_mask) if block_mask is not None else None
-    st = lib().paged_attn_fwd(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), block_table.data_ptr(),
-                              seq_lens.data_ptr(), query_start_loc.data_ptr(),
-                              ctypes.byref(mt) if mt is not None else None,
-                              ctypes.byref(sc) if sc is not None else None, ctypes.byref(ot),
-                              ctypes.byref(lt), ctypes.byref(params), workspace.data_ptr(),
-                              workspace.numel(), ctypes.c_void_p(stream))
+    common = (ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), block_table.data_ptr(),
+              seq_lens.data_ptr(), query_start_loc.data_ptr(), ctypes.byref(mt) if mt is not None else None,
+              ctypes.byref(sc) if sc is not None else None, ctypes.byref(ot), ctypes.byref(lt),
+              ctypes.byref(params))
+    st = lib().paged_attn_fwd(*common, workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream))
     _check(st, "paged_attn_fwd")
     return out, lse, workspace
 

@@ -85,6 +85,18 @@ pa_status check_params(const pa_params* p) {
   return PA_OK;
 }
 
+// Which build of the attention kernel a call runs: without the prefill path
+// when every Q-block is known to be small (a static split, or max_q_len * G
+// <= 16), without the decode path when every one is known to be large
+// (min_q_len * G > 16), else the general one.
+int kernel_paths(const pa_params* p) {
+  const int64_t G = p->num_q_heads / p->num_kv_heads;
+  if (p->split_mode == PA_SPLIT_STATIC || (p->max_q_len > 0 && p->max_q_len * G <= pa::kSmallMaxRows))
+    return 1;
+  if (p->min_q_len * G > pa::kSmallMaxRows) return 2;
+  return 0;
+}
+
 pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   pa_status st = check_params(p);
   if (st != PA_OK) return st;
@@ -96,7 +108,11 @@ pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   const int G = p->num_q_heads / p->num_kv_heads;
   const int64_t rows_large = (int64_t(p->total_q) * G + pa::kLargeRows - 1) / pa::kLargeRows;
   const int64_t n_qb_max = int64_t(p->num_kv_heads) * (p->num_seqs + rows_large);
-  const int64_t max_slots = p->max_partial_slots ? p->max_partial_slots : 2 * int64_t(P);
+  // P workers cut at most 2P Q-blocks (each range cuts its first and its
+  // last); an odd P whose last worker pair is cut unevenly uses P + 1
+  const int64_t max_slots = p->max_partial_slots ? p->max_partial_slots : 2 * (int64_t(P) + (P & 1));
+  // a partial slot holds the largest Q-block the kernel build can meet
+  const int32_t slot_rows = kernel_paths(p) == 1 ? pa::kSmallMaxRows : pa::kLargeRows;
   if (n_qb_max > (1 << 30) || max_slots > (1 << 24)) return PA_ERR_INVALID_ARG;
   std::memset(L, 0, sizeof(*L));
   size_t off = 0;
@@ -108,12 +124,13 @@ pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   L->slot_base = off;     off = align256(off + size_t(n_qb_max) * 4);
   L->combine_list = off;  off = align256(off + size_t(n_qb_max) * 4);
   L->done = off;          off = align256(off + size_t(n_qb_max) * 4);
-  L->partial_lse = off;   off = align256(off + size_t(max_slots) * pa::kLargeRows * 4);
-  L->partial_o = off;     off = align256(off + size_t(max_slots) * pa::kLargeRows * p->head_dim * 4);
+  L->partial_lse = off;   off = align256(off + size_t(max_slots) * slot_rows * 4);
+  L->partial_o = off;     off = align256(off + size_t(max_slots) * slot_rows * p->head_dim * 4);
   L->total = off;
   L->n_qb_max = int32_t(n_qb_max);
   L->max_slots = int32_t(max_slots);
   L->num_workers = P;
+  L->slot_rows = slot_rows;
   return PA_OK;
 }
 
@@ -135,6 +152,33 @@ pa_status check_tensor(const pa_tensor* t, int rank, int dtype, bool rows16) {
       if ((t->stride[i] * es) % 16) return PA_ERR_INVALID_ARG;
   }
   return PA_OK;
+}
+
+// The launches of one call on `stream`: Assign (or the static split's
+// header reset), the attention kernel, and Combine unless it is fused or the
+// static split has one split per Q-block.  ev, when given, receives an event
+// before each launch and one after the last.
+hipError_t launch_all(const pa::KParams& kp, const pa_params& P, const pa_workspace_layout& L, int kind,
+                      int paths, hipStream_t stream, hipEvent_t* ev) {
+  const bool is_static = P.split_mode == PA_SPLIT_STATIC;
+  const int64_t n_static_qb = int64_t(P.num_seqs) * P.num_kv_heads;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+  e = is_static ? pa::launch_static_begin(kp, stream) : pa::launch_assign(kp, stream);
+  if (e != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  const int64_t n_items = n_static_qb * P.static_splits;
+  const int grid = is_static ? static_cast<int>(std::min<int64_t>(n_items, L.num_workers)) : L.num_workers;
+  e = pa::launch_attention(kp, kind, grid, paths, stream);
+  if (e != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+  if (!P.fused_combine && (!is_static || P.static_splits > 1)) {
+    const int cgrid = is_static ? static_cast<int>(std::min<int64_t>(n_static_qb, L.num_workers)) : L.num_workers;
+    e = pa::launch_combine(kp, kind == pa::KIND_F32, cgrid, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -284,12 +328,15 @@ pa_status paged_attn_kernel_timing_read(float* ms_assign, float* ms_attention, f
   return st;
 }
 
-pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
-                         const int32_t* block_table, const int32_t* seq_lens,
-                         const int32_t* query_start_loc, const pa_tensor* block_mask,
-                         const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
-                         const pa_params* params, void* workspace, size_t workspace_bytes,
-                         void* stream_ptr) {
+}  // extern "C"
+
+namespace {
+
+// The whole call on a given workspace.
+pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* query_start_loc,
+                   const pa_tensor* block_mask, const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
+                   const pa_params* params, void* workspace, size_t workspace_bytes, void* stream_ptr) {
   pa_workspace_layout L;
   pa_status st = layout_of(params, &L);
   if (st != PA_OK) return st;
@@ -378,12 +425,10 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   kp.static_S = is_static ? P.static_splits : 0;
   kp.max_q_len = P.max_q_len;
   kp.min_q_len = P.min_q_len;
-  // the kernel build: without the prefill path when every Q-block is known to
-  // be small, without the decode path when every one is known to be large
-  const bool small_only = is_static || (P.max_q_len > 0 && int64_t(P.max_q_len) * kp.G <= pa::kSmallMaxRows);
-  const bool large_only = !small_only && int64_t(P.min_q_len) * kp.G > pa::kSmallMaxRows;
-  kp.pair_w = P.pair_weight ? P.pair_weight : (small_only ? PA_PAIR_WEIGHT_SMALL : PA_PAIR_WEIGHT_GENERAL);
+  const int paths = kernel_paths(params);
+  kp.pair_w = P.pair_weight ? P.pair_weight : (paths == 1 ? PA_PAIR_WEIGHT_SMALL : PA_PAIR_WEIGHT_GENERAL);
   kp.fused = P.fused_combine ? 1 : 0;
+  kp.slot_rows = L.slot_rows;
   char* ws = static_cast<char*>(workspace);
   kp.hdr = reinterpret_cast<int32_t*>(ws + L.header);
   kp.seq_qb_base = reinterpret_cast<int32_t*>(ws + L.seq_qb_base);
@@ -400,38 +445,46 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
 
   TimedCall tc;
+  int n_events = 0;
   bool timing;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     timing = g_timing;
   }
+  // events of a call that fails are destroyed here; a HIP failure after the
+  // first launch leaves the launches before it enqueued
+  auto fail = [&](hipError_t e) {
+    for (int i = 0; i < n_events; ++i) (void)hipEventDestroy(tc.ev[i]);
+    return hip_fail(e);
+  };
   if (timing) {
     for (auto& ev : tc.ev) {
       hipError_t e = hipEventCreate(&ev);
-      if (e != hipSuccess) return hip_fail(e);
+      if (e != hipSuccess) return fail(e);
+      ++n_events;
     }
   }
-  hipError_t e = hipSuccess;
-  if (timing) (void)hipEventRecord(tc.ev[0], stream);
-  e = is_static ? pa::launch_static_begin(kp, stream) : pa::launch_assign(kp, stream);
-  if (e != hipSuccess) return hip_fail(e);
-  if (timing) (void)hipEventRecord(tc.ev[1], stream);
-  const int64_t n_items = n_static_qb * P.static_splits;
-  const int grid = is_static ? static_cast<int>(std::min<int64_t>(n_items, L.num_workers)) : L.num_workers;
-  e = pa::launch_attention(kp, kind, grid, small_only ? 1 : large_only ? 2 : 0, stream);
-  if (e != hipSuccess) return hip_fail(e);
-  if (timing) (void)hipEventRecord(tc.ev[2], stream);
-  if (!P.fused_combine && (!is_static || P.static_splits > 1)) {
-    const int cgrid = is_static ? static_cast<int>(std::min<int64_t>(n_static_qb, L.num_workers)) : L.num_workers;
-    e = pa::launch_combine(kp, kind == pa::KIND_F32, cgrid, stream);
-    if (e != hipSuccess) return hip_fail(e);
-  }
+  hipError_t e = launch_all(kp, P, L, kind, paths, stream, timing ? tc.ev : nullptr);
+  if (e != hipSuccess) return fail(e);
   if (timing) {
-    (void)hipEventRecord(tc.ev[3], stream);
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timed.push_back(tc);
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, const pa_tensor* block_mask,
+                         const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
+                         const pa_params* params, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return fwd_impl(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, block_mask, scales, out, lse,
+                  params, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

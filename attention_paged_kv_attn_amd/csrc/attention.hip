@@ -34,6 +34,7 @@
 //    LDS in MFMA-operand order and double-buffered.
 // Block-sparse prefill compacts the active tiles of a Q-block with a 64-lane
 // ballot + mbcnt prefix into an LDS list ("Triton-TLE ...", §2.1).
+#include <atomic>
 #include <type_traits>
 
 #include "combine_core.h"
@@ -625,18 +626,18 @@ __device__ __forceinline__ void write_row(const KParams& p, const QBlock& x, int
             u32x2{pack_bf16x2(acc[md][0] * inv_l, acc[md][1] * inv_l), pack_bf16x2(acc[md][2] * inv_l, acc[md][3] * inv_l)};
       if (h == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
     } else {
-      float* o = p.part_o + ((int64_t)slot * kLargeRows + r) * D;
+      float* o = p.part_o + ((int64_t)slot * p.slot_rows + r) * D;
       if (p.fused) {
 #pragma unroll
         for (int md = 0; md < MD; ++md)
 #pragma unroll
           for (int i = 0; i < 4; ++i) store_coherent(o + out_dim<KIND, D, true>(h, 0, md) + i, acc[md][i] * inv_l);
-        if (h == 0) store_coherent(p.part_lse + slot * kLargeRows + r, lse);
+        if (h == 0) store_coherent(p.part_lse + slot * p.slot_rows + r, lse);
       } else {
 #pragma unroll
         for (int md = 0; md < MD; ++md)
           *reinterpret_cast<f32x4*>(o + out_dim<KIND, D, true>(h, 0, md)) = acc[md] * inv_l;
-        if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+        if (h == 0) p.part_lse[slot * p.slot_rows + r] = lse;
       }
     }
     return;
@@ -667,19 +668,19 @@ __device__ __forceinline__ void write_row(const KParams& p, const QBlock& x, int
     }
     if (h == 0) p.lse[tok * p.l_st + head * p.l_sh] = lse;
   } else {
-    float* o = p.part_o + ((int64_t)slot * kLargeRows + r) * D;
+    float* o = p.part_o + ((int64_t)slot * p.slot_rows + r) * D;
     if (p.fused) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int md = 0; md < MD; ++md) store_coherent(o + out_dim<KIND, D>(h, j, md), acc[md][j] * inv_l);
-      if (h == 0) store_coherent(p.part_lse + slot * kLargeRows + r, lse);
+      if (h == 0) store_coherent(p.part_lse + slot * p.slot_rows + r, lse);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int md = 0; md < MD; ++md) o[out_dim<KIND, D>(h, j, md)] = acc[md][j] * inv_l;
-      if (h == 0) p.part_lse[slot * kLargeRows + r] = lse;
+      if (h == 0) p.part_lse[slot * p.slot_rows + r] = lse;
     }
   }
 }
@@ -961,14 +962,21 @@ template <int KIND, int D>
 __device__ void finish_split(const KParams& p, int q, const QBlock& x, int ns, int sb) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int last;
-  // the partial went out with device-coherent stores: once they are complete
-  // (all of this thread's memory operations), the counter may move
+  // Publication: every thread's partial stores (device-coherent) are complete
+  // before the barrier, and after it one thread counts the piece with an
+  // agent-scope release; the workgroup that brings the count to ns acquires
+  // at agent scope before it reads the other pieces.  (Release and acquire
+  // order the counter against the pieces in the memory model; the waits make
+  // the other waves' stores part of what the release publishes.)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(p.done + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+    last = __hip_atomic_fetch_add(p.done + q, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
   __syncthreads();
-  if (last) merge_qblock<D, KIND == KIND_F32, true>(p, x, ns, sb, reinterpret_cast<MergeState*>(smem));
+  if (last) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_qblock<D, KIND == KIND_F32, true>(p, x, ns, sb, reinterpret_cast<MergeState*>(smem));
+  }
   __syncthreads();
 }
 
@@ -1092,14 +1100,14 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
       }
       if (d0 == 0) p.lse[tk * p.l_st + hd * p.l_sh] = lse;
     } else {
-      float* dst = p.part_o + ((int64_t)slot * kLargeRows + row) * D + d0;
+      float* dst = p.part_o + ((int64_t)slot * p.slot_rows + row) * D + d0;
       if (p.fused) {
         for (int i = 0; i < 8; ++i) store_coherent(dst + i, o[i] * inv);
-        if (d0 == 0) store_coherent(p.part_lse + slot * kLargeRows + row, lse);
+        if (d0 == 0) store_coherent(p.part_lse + slot * p.slot_rows + row, lse);
       } else {
         *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-        if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+        if (d0 == 0) p.part_lse[slot * p.slot_rows + row] = lse;
       }
     }
   }
@@ -1411,14 +1419,14 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
         }
         if (d0 == 0) p.lse[tk * p.l_st + hd * p.l_sh] = lse;
       } else {
-        float* dst = p.part_o + ((int64_t)slot * kLargeRows + row) * D + d0;
+        float* dst = p.part_o + ((int64_t)slot * p.slot_rows + row) * D + d0;
         if (p.fused) {
           for (int i = 0; i < 8; ++i) store_coherent(dst + i, o[i] * inv);
-          if (d0 == 0) store_coherent(p.part_lse + slot * kLargeRows + row, lse);
+          if (d0 == 0) store_coherent(p.part_lse + slot * p.slot_rows + row, lse);
         } else {
           *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-          if (d0 == 0) p.part_lse[slot * kLargeRows + row] = lse;
+          if (d0 == 0) p.part_lse[slot * p.slot_rows + row] = lse;
         }
       }
     }
@@ -2199,15 +2207,22 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   }
 }
 
+// The dynamic-LDS limit of a kernel build is raised once per device (the
+// attribute is per device); the bit of a device is set only after the call
+// succeeded, and concurrent first calls merely repeat the idempotent set.
 template <int KIND, int D, bool FAST, int PATHS>
 static hipError_t launch_attention_t(const KParams& p, int grid, hipStream_t stream) {
   const int lds = Lds<KIND, D, FAST>::DYN;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST, PATHS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (!bit || !(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attention_kernel<KIND, D, FAST, PATHS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL((attention_kernel<KIND, D, FAST, PATHS>), dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();

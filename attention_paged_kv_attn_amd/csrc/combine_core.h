@@ -107,9 +107,9 @@ __device__ __forceinline__ void merge_qblock(const KParams& p, const QBlock& x, 
     for (int k = 0; k < 8; ++k) st.o[k] = 0.f;
     if (live) {
       for (int sp = grp; sp < ns; sp += groups) {
-        const float* lp = p.part_lse + (sb + sp) * kLargeRows + row;
+        const float* lp = p.part_lse + (sb + sp) * p.slot_rows + row;
         const float ls = COHERENT ? load_coherent(lp) : *lp;
-        merge_part<COHERENT>(st, ls, p.part_o + ((int64_t)(sb + sp) * kLargeRows + row) * D + d0);
+        merge_part<COHERENT>(st, ls, p.part_o + ((int64_t)(sb + sp) * p.slot_rows + row) * D + d0);
       }
     }
     if (groups > 1) {

@@ -58,6 +58,7 @@ struct KParams {
   int32_t min_q_len; // > 0: the caller's bound below every non-zero q_len (checked by Assign)
   int32_t pair_w;    // percent of a worker pair's 2L units given to its first worker
   int32_t fused;     // 1: the last workgroup to finish a split Q-block merges it (no Combine launch)
+  int32_t slot_rows; // rows per partial slot: the kernel build's largest Q-block (16 or 128)
   // workspace
   int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
   int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;

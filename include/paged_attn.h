@@ -34,7 +34,8 @@
  *    synchronises, never reads device memory on the host and keeps no pointer
  *    after a call returns.  The caller owns every buffer, the workspace
  *    included.  All argument checks run before the first launch: a call that
- *    fails has no side effects.
+ *    fails a check has no side effects; a HIP runtime failure (PA_ERR_HIP)
+ *    may leave the launches issued before it enqueued.
  *  - Calls are re-entrant; two calls that share a workspace must be ordered
  *    on one stream.
  */
@@ -120,7 +121,7 @@ typedef struct pa_params {
   int32_t num_workers;          /* P persistent workgroups; 0 = two per compute unit */
   int32_t split_min_units;      /* L_min: fewest 64-key units a worker is given; 0 = 8 */
   int32_t force_split_units;    /* > 0: every worker gets exactly this many units (testing) */
-  int32_t max_partial_slots;    /* capacity for split partial outputs; 0 = 2 * P */
+  int32_t max_partial_slots;    /* capacity for split partial outputs; 0 = 2 * P (2 * (P + 1) for an odd P) */
   int32_t flags;                /* reserved, must be 0 */
   int32_t split_mode;           /* pa_split_mode */
   int32_t static_splits;        /* PA_SPLIT_STATIC: S >= 1 splits per Q-block */
@@ -184,12 +185,14 @@ typedef struct pa_workspace_layout {
   size_t slot_base;       /* int32[n_qb_max], -1 when not split */
   size_t combine_list;    /* int32[n_qb_max] */
   size_t done;            /* int32[n_qb_max]: finished pieces per split Q-block (fused Combine) */
-  size_t partial_lse;     /* float[max_slots][128] */
-  size_t partial_o;       /* float[max_slots][128][head_dim] */
+  size_t partial_lse;     /* float[max_slots][slot_rows] */
+  size_t partial_o;       /* float[max_slots][slot_rows][head_dim] */
   size_t total;           /* bytes needed */
   int32_t n_qb_max;
   int32_t max_slots;
   int32_t num_workers;
+  int32_t slot_rows;      /* rows per partial slot: 16 when every Q-block is known to be small
+                             (PA_SPLIT_STATIC, or max_q_len * Hq / Hkv <= 16), else 128 */
 } pa_workspace_layout;
 
 typedef struct pa_device_info {
@@ -223,12 +226,18 @@ typedef enum pa_device_error {
  *  v_cache      dim) with free strides on the first three dims, so an NHD
  *               cache [pages, slot, head, d] and an HND cache
  *               [pages, head, slot, d] are both passed by permuting strides.
- *               Same dtype as q.  Only slots j < seq_len of each sequence are
- *               read; other slots may hold anything (NaN included).
+ *               Same dtype as q.  Keys j >= seq_len of a sequence never
+ *               affect a result and may hold anything (NaN included); with
+ *               page_size >= 64 the rest of the 64-slot tile holding a
+ *               sequence's last key is read (and discarded), so those slots
+ *               must be addressable memory of the cache, as they are.
  *  block_table  int32 [B, max_pages_per_seq] (row stride
  *               params->block_table_stride); entry [b, j / page_size] is the
  *               physical page of key j of sequence b.  Entries past a
- *               sequence's last page are never read.
+ *               sequence's last page may be read (the page-table window of a
+ *               sequence covers up to 128 entries, clamped to
+ *               max_pages_per_seq - 1) but never affect a result, so they
+ *               may hold anything (e.g. -1).
  *  seq_lens     int32 [B]: keys of each sequence, counting its new tokens.
  *  query_start_loc int32 [B + 1]: query rows of sequence b are
  *               [qsl[b], qsl[b+1]); token i of the q_len = qsl[b+1] - qsl[b]
@@ -255,10 +264,20 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          void* stream);
 
 /* Bytes of workspace paged_attn_fwd needs for `params` (host only; queries the
- * current device's compute-unit count when params->num_workers is 0). */
+ * current device's compute-unit count when params->num_workers is 0).  The
+ * caller allocates it once and passes it to every call: a closed form on the
+ * host, so no call allocates or frees memory ("HiLS-Attention sliding-window
+ * forward", §3 stage 3: per-call allocation and lookup made up most of a
+ * wrapper's time around a short kernel).  Decode-only calls (max_q_len * G
+ * <= 16, or PA_SPLIT_STATIC) need 16-row partial slots, others 128-row. */
 pa_status paged_attn_workspace_size(const pa_params* params, size_t* bytes);
 
-/* Offsets of the task map inside the workspace (host only). */
+/* Offsets of the task map inside the workspace (host only), for tests that
+ * copy the workspace to the host and compare the Assign task map ("Triton-TLE
+ * rewrite of Tencent HPC-Ops Attention", §1.2 and §3.3) bit for bit with a
+ * CPU specification.  It takes the place of a call that would decode the map
+ * itself: the map is plain int32 arrays, so their offsets are all a reader
+ * needs. */
 pa_status paged_attn_workspace_layout(const pa_params* params, pa_workspace_layout* layout);
 
 /* The split policy: picks PA_SPLIT_STATIC (and its S) or PA_SPLIT_DYNAMIC
@@ -282,14 +301,22 @@ pa_status paged_attn_plan_split(const pa_params* params, const int32_t* seq_lens
 /* Host-side check of batch metadata held in host memory: query_start_loc is a
  * prefix ending at total_q, 0 <= q_len <= seq_len, every block_table entry a
  * sequence needs is in [0, num_pages), and (when block_mask_h is given, a
- * dense [B, mask_heads, n_q_tiles, n_k_tiles] array) the mask covers every
- * sequence.  Runs no device code. */
+ * dense [B, mask_heads, n_q_tiles, n_k_tiles] array, its three trailing
+ * dimensions passed as mask_heads / mask_q_tiles / mask_k_tiles since a host
+ * pointer carries no shape) the mask covers every sequence.  The rules are
+ * those of the paged layout and varlen packing ("Triton-TLE rewrite of
+ * Tencent HPC-Ops Attention", §1.2 block table, §3.2 logical page / slot
+ * coordinates).  Runs no device code; paged_attn_fwd itself never reads host
+ * copies and checks the same rules on the device (error word). */
 pa_status paged_attn_validate_host(const pa_params* params, const int32_t* seq_lens_h,
                                    const int32_t* query_start_loc_h, const int32_t* block_table_h,
                                    const uint8_t* block_mask_h, int32_t mask_heads,
                                    int32_t mask_q_tiles, int32_t mask_k_tiles);
 
-/* Compute units, LDS per workgroup and the default worker count of `device`. */
+/* Compute units, LDS per workgroup and the default worker count of `device`:
+ * the persistent grid is sized to the machine, not to the batch ("vLLM
+ * Triton Attention Backend Deep Dive", §3: a fixed grid reading its work from
+ * GPU metadata), two workgroups per compute unit. */
 pa_status paged_attn_device_info(int32_t device, pa_device_info* info);
 
 /* Static text for a status code. */

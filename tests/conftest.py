@@ -29,3 +29,9 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+def pytest_terminal_summary(terminalreporter):
+    from tests import parity_log
+    for line in parity_log.summary_lines():
+        terminalreporter.write_line(line)

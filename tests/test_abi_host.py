@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for s in range(5):
-        assert B.paged_attn_status_string(s)
+        assert B.paged_attn_status_string(s) != "unknown status"
     assert B.paged_attn_status_string(0) == "ok"
 
 
@@ -53,9 +53,29 @@ def test_workspace_size_closed_form():
     offs = [lay.header, lay.seq_qb_base, lay.qb_desc, lay.unit_prefix, lay.n_splits, lay.slot_base,
             lay.combine_list, lay.partial_lse, lay.partial_o, lay.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.slot_rows == 128                  # the general kernel build: 128-row Q-blocks
     # monotone in the sizes that drive it
     assert B.paged_attn_workspace_size(_params(total_q=4096)) > lay.total
     assert B.paged_attn_workspace_size(_params(num_workers=1024)) > lay.total
+
+
+def test_partial_slots_follow_the_kernel_build():
+    """A call whose Q-blocks are all known to be small (max_q_len * G <= 16, or
+    a static split) gets 16-row partial slots; otherwise slots hold 128 rows."""
+    for kw, rows in ((dict(max_q_len=4), 16), (dict(max_q_len=5), 128), (dict(min_q_len=32), 128),
+                     (dict(split_mode=B.PA_SPLIT_STATIC, static_splits=2), 16), ({}, 128)):
+        lay = B.paged_attn_workspace_layout(_params(**kw))
+        assert lay.slot_rows == rows, kw
+        assert lay.partial_o - lay.partial_lse >= lay.max_slots * rows * 4
+        assert lay.total - lay.partial_o >= lay.max_slots * rows * 128 * 4
+    small = B.paged_attn_workspace_size(_params(max_q_len=1))
+    assert small < B.paged_attn_workspace_size(_params()) // 4
+
+
+def test_odd_worker_count_gets_slots_for_one_more_worker():
+    assert B.paged_attn_workspace_layout(_params(num_workers=7)).max_slots == 16
+    assert B.paged_attn_workspace_layout(_params(num_workers=8)).max_slots == 16
+    assert B.paged_attn_workspace_layout(_params(num_workers=7, max_partial_slots=5)).max_slots == 5
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=96), dict(num_kv_heads=5), dict(page_size=48),
