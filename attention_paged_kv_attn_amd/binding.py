@@ -27,7 +27,9 @@ PA_PAIR_WEIGHT_SMALL, PA_PAIR_WEIGHT_GENERAL = 60, 50
 EXPORTS = ("paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_workspace_layout",
            "paged_attn_validate_host", "paged_attn_device_info", "paged_attn_status_string",
            "paged_attn_last_hip_error", "paged_attn_kernel_timing", "paged_attn_kernel_timing_read",
-           "paged_attn_plan_split")
+           "paged_attn_plan_split", "paged_attn_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 72 << 20
+PA_ERR_SCRATCH = 5
 
 
 class pa_tensor(ctypes.Structure):
@@ -79,6 +81,9 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_void_p, ctypes.c_void_p, P(pa_tensor), P(pa_scales),
                                      P(pa_tensor), P(pa_tensor), P(pa_params), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
+        L.paged_attn_fwd_noalloc.argtypes = [P(pa_tensor), P(pa_tensor), P(pa_tensor), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, P(pa_tensor), P(pa_scales),
+                                             P(pa_tensor), P(pa_tensor), P(pa_params), ctypes.c_void_p]
         L.paged_attn_workspace_size.argtypes = [P(pa_params), P(ctypes.c_size_t)]
         L.paged_attn_workspace_layout.argtypes = [P(pa_params), P(pa_workspace_layout)]
         L.paged_attn_validate_host.argtypes = [P(pa_params), ctypes.c_void_p, ctypes.c_void_p,
@@ -242,8 +247,12 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    block_mask_tile: int = 128, num_workers: int = 0, split_min_units: int = 0,
                    force_split_units: int = 0, max_partial_slots: int = 0, split: str = "dynamic",
                    static_splits: int = 0, max_q_len: int = 0, min_q_len: int = 0, pair_weight: int = 0,
-                   fused_combine: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+                   fused_combine: bool = False, workspace: Optional[torch.Tensor] = None, stream=None,
+                   noalloc: bool = False):
     """Run the library on torch tensors; returns (out, lse, workspace).
+
+    noalloc: call paged_attn_fwd_noalloc (the library's own scratch array is
+    the workspace; `workspace` must be None and None is returned for it).
 
     q [total_q, Hq, d]; k_cache/v_cache NHD [pages, page_size, Hkv, d] or HND
     [pages, Hkv, page_size, d]; block_table int32 [B, max_pages]; seq_lens int32
@@ -286,9 +295,13 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         out = torch.empty((total_q, Hq, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
-    need = paged_attn_workspace_size(params)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("the no-allocation entry point takes no workspace")
+    else:
+        need = paged_attn_workspace_size(params)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     sc = None
     if scales is not None:
         sc = pa_scales()
@@ -311,6 +324,9 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
               seq_lens.data_ptr(), query_start_loc.data_ptr(), ctypes.byref(mt) if mt is not None else None,
               ctypes.byref(sc) if sc is not None else None, ctypes.byref(ot), ctypes.byref(lt),
               ctypes.byref(params))
+    if noalloc:
+        _check(lib().paged_attn_fwd_noalloc(*common, ctypes.c_void_p(stream)), "paged_attn_fwd_noalloc")
+        return out, lse, None
     st = lib().paged_attn_fwd(*common, workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream))
     _check(st, "paged_attn_fwd")
     return out, lse, workspace

@@ -5,6 +5,7 @@
 #include <cmath>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -192,6 +193,7 @@ const char* paged_attn_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_SCRATCH: return "problem needs more workspace than the no-allocation entry point holds";
   }
   return "unknown status";
 }
@@ -332,11 +334,14 @@ pa_status paged_attn_kernel_timing_read(float* ms_assign, float* ms_attention, f
 
 namespace {
 
-// The whole call on a given workspace.
+// The whole call on a given workspace.  from_scratch: the workspace is the
+// library's own scratch array (the no-allocation entry point), which reports a
+// problem too large for it as PA_ERR_SCRATCH and records no timing events.
 pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
                    const int32_t* block_table, const int32_t* seq_lens, const int32_t* query_start_loc,
                    const pa_tensor* block_mask, const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
-                   const pa_params* params, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+                   const pa_params* params, void* workspace, size_t workspace_bytes, void* stream_ptr,
+                   bool from_scratch) {
   pa_workspace_layout L;
   pa_status st = layout_of(params, &L);
   if (st != PA_OK) return st;
@@ -383,7 +388,7 @@ pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor
     if (n_static_qb * P.static_splits > (1 << 30)) return PA_ERR_INVALID_ARG;
   }
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;
-  if (workspace_bytes < L.total) return PA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total) return from_scratch ? PA_ERR_SCRATCH : PA_ERR_WORKSPACE;
   if (P.total_q == 0) return PA_OK;
 
   pa::KParams kp;
@@ -446,8 +451,8 @@ pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor
 
   TimedCall tc;
   int n_events = 0;
-  bool timing;
-  {
+  bool timing = false;
+  if (!from_scratch) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     timing = g_timing;
   }
@@ -473,6 +478,40 @@ pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor
   return PA_OK;
 }
 
+// The library's own workspace for callers that cannot allocate.  In host code
+// the name stands for the array only symbolically; its device address (one
+// copy per device) comes from hipGetSymbolAddress, once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The scratch array's address on the current device (looked up on the first
+// call there, with that device current, and kept).
+pa_status scratch_on_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -484,7 +523,19 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          const pa_params* params, void* workspace, size_t workspace_bytes,
                          void* stream) {
   return fwd_impl(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, block_mask, scales, out, lse,
-                  params, workspace, workspace_bytes, stream);
+                  params, workspace, workspace_bytes, stream, false);
+}
+
+pa_status paged_attn_fwd_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, const pa_tensor* block_mask,
+                                 const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
+                                 const pa_params* params, void* stream) {
+  void* ws = nullptr;
+  const pa_status st = scratch_on_current_device(&ws);
+  if (st != PA_OK) return st;
+  return fwd_impl(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, block_mask, scales, out, lse,
+                  params, ws, PA_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 }  // extern "C"

@@ -54,7 +54,9 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent shape/stride, bad size */
   PA_ERR_UNSUPPORTED = 2,   /* dtype mix, head_dim, GQA ratio or layout not built */
   PA_ERR_WORKSPACE = 3,     /* workspace null, misaligned or too small */
-  PA_ERR_HIP = 4            /* a HIP runtime call failed; see paged_attn_last_hip_error */
+  PA_ERR_HIP = 4,           /* a HIP runtime call failed; see paged_attn_last_hip_error */
+  PA_ERR_SCRATCH = 5        /* paged_attn_fwd_noalloc: the call needs more workspace than
+                               PA_NOALLOC_SCRATCH_BYTES */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -262,6 +264,32 @@ pa_status paged_attn_fwd(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
                          const pa_params* params, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* paged_attn_fwd_noalloc — paged_attn_fwd for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  The arguments and results are those of
+ * paged_attn_fwd without workspace / workspace_bytes: the workspace is instead
+ * a library-owned device array of PA_NOALLOC_SCRATCH_BYTES (256-byte aligned),
+ * one per device, present from the library's load on that device until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up the
+ * array's address there.  A call whose paged_attn_workspace_size exceeds
+ * PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH before any launch.  On a
+ * 256-CU device with the default 512 workers, d = 128 and 128-row partial
+ * slots, the slots take 64.5 MiB and the rest holds the task map of about
+ * 150,000 Q-blocks (n_qb_max = Hkv * (B + ceil(total_q * Hq / Hkv / 128)));
+ * a small-Q-block call (16-row slots) needs about 8 MiB for its slots.
+ * Every call on one device shares that
+ * device's array and leaves the previous call's task map in it (each call
+ * rewrites all it reads): calls that overlap in time on one device race and
+ * must be ordered on one stream.  Kernel timing (paged_attn_kernel_timing)
+ * records no events for this entry point. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+pa_status paged_attn_fwd_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, const pa_tensor* block_mask,
+                                 const pa_scales* scales, pa_tensor* out, pa_tensor* lse,
+                                 const pa_params* params, void* stream);
 
 /* Bytes of workspace paged_attn_fwd needs for `params` (host only; queries the
  * current device's compute-unit count when params->num_workers is 0).  The

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert B.paged_attn_status_string(s) != "unknown status"
     assert B.paged_attn_status_string(0) == "ok"
 
