@@ -6,8 +6,18 @@ over one batch whose inputs already sit in HBM.  The headline workload is the
 dynamic split-K decode batch with the Llama-3.1-8B attention shape (Hq 32,
 Hkv 8, d 128, bf16, 64 sequences with log-uniform contexts 128..32768, 64-token
 pages in a random permutation, q_len 1, NHD); its metric is algorithmic HBM
-GB/s.  A second leg times the bf16 dense causal prefill at the FP8-prefill
-shape (2 x 8192 tokens) for TFLOP/s against the MFMA peak.
+GB/s, and the same step is also timed replayed from a HIP graph.  The
+`prefill` leg times the bf16 dense causal prefill at the FP8-prefill shape
+(2 x 8192 tokens) for TFLOP/s against the MFMA peak.  The `also` legs cover
+the other workloads: the decode batch in HND, at q_len 2 and 4 and in fp8;
+the hybrid chunked step; FP8 prefill dense and block-sparse (tile-skip ratio,
+speed-up over its dense run); the sliding-window forward; the windowed and
+full 128K decodes under the split policy.  Every leg carries a roofline
+object for its attention kernel (HBM or MFMA bound); legs whose working set
+is under 1 GB read a 1 GiB buffer between timed steps so their data comes
+from HBM.  A streaming-bandwidth figure of torch's own kernels and the fp64
+oracle timed on the host's cores (decode batch and sampled prefill rows)
+give context.
 
 Prints ONE JSON line.  Progress goes to stderr.
 """
@@ -148,7 +158,28 @@ def split_kw(spec, g):
     raise ValueError(spec)
 
 
-def time_graph(g, kw, steps, warmup):
+# attention-kernel launches per leg, in execution order (the kernel-trace
+# summary slices the trace by these counts)
+LAUNCH_LOG = []
+_FLUSH = None
+FLUSH_BYTES = 1 << 30
+FLUSH_BELOW_BYTES = 1_000_000_000
+
+
+def flush_caches():
+    """Read a 1 GiB scratch buffer: evicts the L2s and the 256 MiB MALL with
+    clean lines, so a working set under 1 GB is read from HBM on every timed
+    step.  (Writing the buffer instead leaves up to the MALL's size in dirty
+    lines, whose write-back then runs inside the next timed kernel: measured
+    0.156 -> 0.219 ms on the 0.7 GB fp8 decode batch.)"""
+    import torch
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    _FLUSH.sum()
+
+
+def time_graph(g, kw, steps, warmup, leg_name):
     """The step captured once in a HIP graph, then replayed: ms per replay."""
     import torch
     from attention_paged_kv_attn_amd import binding as B
@@ -169,17 +200,21 @@ def time_graph(g, kw, steps, warmup):
         graph.replay()
     t1.record()
     torch.cuda.synchronize()
+    LAUNCH_LOG.append((leg_name, 1 + 2 * warmup + steps, steps))
     return t0.elapsed_time(t1) / steps
 
 
-def time_workload(batch, steps, warmup, split=None):
+def time_workload(batch, steps, warmup, split=None, flush=False, leg_name=None, g=None):
+    """Eager steps: returns (ms per step, per-kernel ms, flushed).  With
+    `flush`, a 1 GiB write runs before every timed step, outside its events."""
     import torch
     from attention_paged_kv_attn_amd import binding as B
-    g = batch.to("cuda:0")
+    g = batch.to("cuda:0") if g is None else g
+    leg_name = leg_name or batch.name
     if split and split.endswith("+graph"):
         kw = split_kw(split[:-len("+graph")] or None, g)
-        ms = time_graph(g, kw, steps, warmup)
-        return ms, {"assign": float("nan"), "attention": float("nan"), "combine": float("nan")}, None
+        ms = time_graph(g, kw, steps, warmup, leg_name)
+        return ms, {"assign": float("nan"), "attention": float("nan"), "combine": float("nan")}, False
     kw = split_kw(split, g)
     out, lse, ws = B.run_batch(g, **kw)      # allocates outputs + workspace once
     torch.cuda.synchronize()
@@ -189,46 +224,115 @@ def time_workload(batch, steps, warmup, split=None):
     B.paged_attn_kernel_timing_read()         # clear
     B.paged_attn_kernel_timing(True)
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    if not flush:
+        ev[0][0].record(stream)
+    for i in range(steps):
+        if flush:
+            flush_caches()
+            ev[i][0].record(stream)
         B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
-    t1.record(stream)
+        if flush:
+            ev[i][1].record(stream)
+    if not flush:
+        ev[-1][1].record(stream)
     torch.cuda.synchronize()
     B.paged_attn_kernel_timing(False)
     a, att, c, n = B.paged_attn_kernel_timing_read()
-    ms = t0.elapsed_time(t1) / steps
-    return ms, {"assign": a / n, "attention": att / n, "combine": c / n}, (g, out, lse, ws)
+    if flush:
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+    else:
+        ms = ev[0][0].elapsed_time(ev[-1][1]) / steps
+    LAUNCH_LOG.append((leg_name, 1 + warmup + steps, steps))
+    return ms, {"assign": a / n, "attention": att / n, "combine": c / n}, flush
 
 
-def cpu_baseline(batch, budget_s=12.0):
-    """The oracle, one sequence at a time in batch order (wrapping round), until
-    ~budget_s of CPU work; throughput in the same algorithmic GB/s."""
+def _cpu_threads():
+    """Threads the CPU baseline may use: the machine's CPU share when the launcher
+    states it (OMP_NUM_THREADS), else every core."""
+    return int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return max((int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"),
+               default=1)
+
+
+def cpu_baseline(batch, by, budget_s=10.0):
+    """The oracle over the whole headline batch, repeated until ~budget_s of
+    CPU work, on the host's cores; algorithmic GB/s as the GPU figure."""
+    from threadpoolctl import threadpool_limits
+    from tests.oracle_helpers import run_oracle
+    n = _cpu_threads()
+    t_total, calls = 0.0, 0
+    with threadpool_limits(limits=n):
+        blas = _blas_threads()
+        while t_total < budget_s:
+            t = time.perf_counter()
+            run_oracle(batch)
+            t_total += time.perf_counter() - t
+            calls += 1
+    return {"value": round(by * calls / t_total / 1e9, 3), "unit": "GB/s", "cores": blas, "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "blas_threads": blas,
+            "sample": f"{calls} oracle passes over the whole {batch.name} batch ({batch.num_seqs} sequences, "
+                      f"{int(batch.seq_lens.sum())} keys, {by / 1e9:.3f} GB algorithmic each), fp64 NumPy, "
+                      f"BLAS on {blas} threads, {t_total:.1f} s"}
+
+
+def cpu_baseline_prefill(batch, budget_s=10.0, rows_per_seq=32):
+    """The oracle on sampled query rows of the prefill batch (evenly spaced
+    positions, every head), until ~budget_s; TFLOP/s of the visible work."""
     from threadpoolctl import threadpool_limits
     from tests.oracle_helpers import run_oracle
     qsl = batch.query_start_loc.numpy().astype(np.int64)
-    ctx_all = batch.seq_lens.numpy().astype(np.int64)
-    d, Hq, Hkv = batch.head_dim, batch.num_q_heads, batch.num_kv_heads
-    elt = {"f32": 4, "bf16": 2, "e4m3": 1}[batch.kind]
-    t_total, by, calls, keys = 0.0, 0, 0, 0
-    with threadpool_limits(limits=1):
+    rows = np.zeros(batch.total_q, bool)
+    for b in range(batch.num_seqs):
+        ql = int(qsl[b + 1] - qsl[b])
+        rows[qsl[b] + np.unique(np.linspace(0, ql - 1, rows_per_seq).astype(np.int64))] = True
+    sub_pairs = 0
+    ctx = batch.seq_lens.numpy().astype(np.int64)
+    for b in range(batch.num_seqs):
+        r = np.nonzero(rows[qsl[b]:qsl[b + 1]])[0]
+        sub_pairs += int((ctx[b] - (qsl[b + 1] - qsl[b]) + r + 1).sum())   # causal, no mask
+    flops = 4.0 * batch.head_dim * batch.num_q_heads * sub_pairs
+    n = _cpu_threads()
+    t_total, calls = 0.0, 0
+    with threadpool_limits(limits=n):
+        blas = _blas_threads()
         while t_total < budget_s:
-            s = calls % batch.num_seqs
-            rows = np.zeros(batch.total_q, bool)
-            rows[qsl[s]:qsl[s + 1]] = True
             t = time.perf_counter()
             run_oracle(batch, rows=rows)
             t_total += time.perf_counter() - t
-            nq, c = int(qsl[s + 1] - qsl[s]), int(ctx_all[s])
-            by += c * Hkv * d * elt * 2 + nq * Hq * d * (elt + 2) + nq * Hq * 4 + \
-                (c + batch.page_size - 1) // batch.page_size * 4
-            keys += c
             calls += 1
-    return {"value": round(by / t_total / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} single-sequence oracle calls over the same decode batch in order "
-                      f"({keys} keys, {by / 1e9:.3f} GB algorithmic), fp64 NumPy, BLAS limited to one "
-                      f"thread, {t_total:.1f} s"}
+    return {"value": round(flops * calls / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": blas,
+            "kind": "oracle", "sample": f"{calls} oracle passes over {int(rows.sum())} query rows x "
+                                        f"{batch.num_q_heads} heads of {batch.name} (evenly spaced positions), "
+                                        f"{flops / 1e9:.1f} GFLOP each, BLAS on {blas} threads, {t_total:.1f} s"}
+
+
+def stream_bandwidth():
+    """Context only: torch's own streaming kernels on 2 GiB (a sum reads it,
+    a copy reads and writes it); GB/s of bytes moved."""
+    import torch
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    res = {}
+    for name, fn, moved in (("read_sum", lambda: x.sum(), 4 * n), ("copy", lambda: y.copy_(x), 8 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = round(moved * 10 / (t0.elapsed_time(t1) * 1e-3) / 1e9, 1)
+    del x, y
+    return {"unit": "GB/s", **res, "kernels": "torch sum / copy_ over 2 GiB fp32 (context, not a target)"}
 
 
 WORKLOADS = {
@@ -244,6 +348,8 @@ WORKLOADS = {
     "prefill_bf16_dense": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="bf16", mask=False, poison=False),
     "prefill_fp8_tensor_mask": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="e4m3", quant_mode="tensor", mask=True, poison=False),
     "prefill_fp8_tensor_dense": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="e4m3", quant_mode="tensor", mask=False, poison=False),
+    "prefill_fp8_page_head_mask": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="e4m3", quant_mode="page_head", mask=True, poison=False),
+    "prefill_fp8_page_head_dense": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sparse_prefill(kind="e4m3", quant_mode="page_head", mask=False, poison=False),
     "window_fwd": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sliding_window(poison=False),
     "window_decode_128k_full": lambda: _full_decode_128k(),
     "window_decode_128k": lambda: __import__("attention_paged_kv_attn_amd.workloads", fromlist=["x"]).sliding_window(decode=True, poison=False),
@@ -257,19 +363,66 @@ def _full_decode_128k():
     return b
 
 
+# how each workload is bounded: HBM bytes (decode-like) or MFMA flops (prefill-like)
+MFMA_BOUND = {"prefill_bf16_dense", "prefill_fp8_tensor_dense", "prefill_fp8_tensor_mask",
+              "prefill_fp8_page_head_dense", "prefill_fp8_page_head_mask", "window_fwd"}
+
+# the default run: every config's timing leg after the headline decode and the
+# bf16 dense prefill (C2 MTP and layouts, C2 fp8, C3, C4 fp8, C5 and its decodes)
+DEFAULT_EXTRA = ("splitk_decode_q1_HND,splitk_decode_q2_NHD,splitk_decode_q4_NHD,splitk_decode_fp8_q1_NHD,"
+                 "hybrid_chunked,prefill_fp8_tensor_dense,prefill_fp8_tensor_mask,window_fwd,"
+                 "window_decode_128k@auto,window_decode_128k_full@auto")
+
+
+def roofline_of(name, batch, by, flops, att_ms):
+    """The roofline object of one leg's attention kernel: algorithmic work per
+    launch over its mean launch time (HIP events on the kernel's stream)."""
+    wl = name.partition("@")[0]
+    if wl in MFMA_BOUND:
+        peak = FP8_PEAK_TFLOPS if batch.kind == "e4m3" else BF16_PEAK_TFLOPS
+        ach = flops / (att_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+             "frac": round(ach / peak, 4)}
+    else:
+        ach = by / (att_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4)}
+    r["traffic"] = traffic_for(wl)
+    prof = profile_summary(wl)
+    if prof and prof.get("source_sha") == source_sha() and prof.get("mfma_busy") is not None:
+        r["mfma_busy"] = prof["mfma_busy"]              # rocprof: MFMA busy / (SIMDs x active cycles)
+        r["clock_ghz"] = prof.get("clock_ghz")
+    return r
+
+
 def leg(name, steps, warmup):
     """name is a workload, optionally '@dynamic', '@auto' or '@static<S>', and
     '+graph' to time replays of the step captured in a HIP graph."""
-    name, _, split = name.partition("@")
-    log(f"generating {name}")
-    batch = WORKLOADS[name]()
+    wl, _, split = name.partition("@")
+    log(f"generating {wl}")
+    batch = WORKLOADS[wl]()
     pairs, keys = visible_pairs_and_keys(batch)
     by = algorithmic_bytes(batch, keys)
     flops = 4.0 * batch.head_dim * pairs
-    log(f"{name}: {by / 1e9:.3f} GB algorithmic, {flops / 1e12:.4f} TFLOP; timing {steps} steps")
-    ms, kms, _ = time_workload(batch, steps, warmup, split or None)
-    log(f"{name}@{split or 'dynamic'}: {ms:.4f} ms/step; kernels {kms}")
-    return batch, by, flops, ms, kms
+    flush = by < FLUSH_BELOW_BYTES and not split.endswith("+graph")
+    log(f"{name}: {by / 1e9:.3f} GB algorithmic, {flops / 1e12:.4f} TFLOP; timing {steps} steps"
+        f"{' (caches flushed between steps)' if flush else ''}")
+    ms, kms, flushed = time_workload(batch, steps, warmup, split or None, flush=flush, leg_name=name)
+    log(f"{name}: {ms:.4f} ms/step; kernels {kms}")
+    return batch, by, flops, ms, kms, flushed
+
+
+def leg_entry(name, batch, by, flops, ms, kms, flushed):
+    e = {"workload": name, "ms_per_step": round(ms, 5), "flushed": flushed,
+         "algorithmic_bytes": int(by), "flops": flops}
+    if kms["attention"] == kms["attention"]:            # per-kernel times exist (not a graph replay)
+        e["kernels_ms"] = {k: round(v, 5) for k, v in kms.items()}
+        e["roofline"] = roofline_of(name, batch, by, flops, kms["attention"])
+        e["gbs_attention"] = round(by / (kms["attention"] * 1e-3) / 1e9, 1)
+        e["tflops_attention"] = round(flops / (kms["attention"] * 1e-3) / 1e12, 2)
+    if "tile_skip_ratio" in batch.info:
+        e["tile_skip_ratio"] = round(batch.info["tile_skip_ratio"], 4)
+    return e
 
 
 COPY_CALIBRATION_BYTES = 1 << 30
@@ -305,6 +458,36 @@ def _counter_per_dispatch(directory, counter, name_pred):
     return vals
 
 
+N_XCD, N_CU, N_SIMD = 8, 256, 1024        # MI355X: counters summed over XCDs, SIMDs per device
+
+
+def derive_counters(c, avg_ns):
+    """Utilisations from raw counter sums of one dispatch, by rocprof's own
+    formulas for gfx950 (GRBM_GUI_ACTIVE summed over the 8 XCDs is 8x the
+    per-XCD active cycles)."""
+    out = {}
+    gui = c.get("GRBM_GUI_ACTIVE")
+    if not gui:
+        return out
+    cyc = gui / N_XCD
+    out["active_cycles"] = round(cyc)
+    if avg_ns:
+        out["clock_ghz"] = round(cyc / avg_ns, 3)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc), 4)
+    for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8"):
+        if k in c:
+            out["mfma_flops_" + k.rsplit("_", 1)[1].lower()] = c[k] * 512
+    if "SQ_ACTIVE_INST_VALU" in c:
+        out["valu_active"] = round(c["SQ_ACTIVE_INST_VALU"] / (N_CU * cyc), 4)
+    if "SQ_LDS_IDX_ACTIVE" in c:
+        out["lds_idx_active"] = round(c["SQ_LDS_IDX_ACTIVE"] / (N_CU * cyc), 4)
+        if "SQ_LDS_BANK_CONFLICT" in c:
+            out["lds_bank_conflict_ratio"] = round(c["SQ_LDS_BANK_CONFLICT"] /
+                                                   max(1.0, c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"]), 4)
+    return out
+
+
 def summarize_profiles(d):
     """Turn the rocprofv3 CSV output of the profiling commands (listed in
     <d>/commands.txt) into the text summaries under profiles/."""
@@ -322,48 +505,41 @@ def summarize_profiles(d):
     with open(os.path.join(out_dir, "copy_calibration.md"), "w") as f:
         f.write("# FETCH_SIZE / WRITE_SIZE calibration on a plain copy kernel\n\n")
         f.write(f"Copy of {COPY_CALIBRATION_BYTES} bytes (1 GiB), {len(cf)} dispatches.\n\n")
-        f.write(f"| counter | median KiB per dispatch | bytes it stands for | scale |\n|---|---|---|---|\n")
+        f.write("| counter | median KiB per dispatch | bytes it stands for | scale |\n|---|---|---|---|\n")
         f.write(f"| FETCH_SIZE | {cf_med:.1f} | {COPY_CALIBRATION_BYTES} | {f_scale:.4f} |\n")
         f.write(f"| WRITE_SIZE | {cw_med:.1f} | {COPY_CALIBRATION_BYTES} | {w_scale:.4f} |\n\n")
-        f.write("Commands:\n\n```\n" + cmds + "\n```\n")
-    # full kernel stats of the default bench command
+        f.write("Commands:\n\n```\n" + "\n".join(c for c in cmds.splitlines() if "copy" in c) + "\n```\n")
+    # the kernel trace of the default bench command, split by its launch log
     stats = _csv_rows(os.path.join(d, "trace"), "kernel_stats.csv")
     trace = _csv_rows(os.path.join(d, "trace"), "kernel_trace.csv")
     bench_line = [json.loads(x) for x in open(os.path.join(d, "bench_trace.json")).read().splitlines()
                   if x.startswith("{")][-1]
-    att = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-           for r in trace if is_att(r["Kernel_Name"])]
-    att.sort()
-    steps, warmup = bench_line["steps"], bench_line["warmup"]
-    n_dec = 1 + warmup + steps                       # run_batch once, warmup, timed steps
-    legs = {bench_line["config"]["workload"]: att[:n_dec]}
-    off = n_dec
+    att = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                 for r in trace if is_att(r["Kernel_Name"]))
     events = {bench_line["config"]["workload"]: bench_line["kernels_ms"]["attention"]}
-    n_leg = 1 + warmup + max(5, steps // 2)
-    if "prefill" in bench_line:
-        legs[bench_line["prefill"]["workload"]] = att[off:off + n_leg]
-        events[bench_line["prefill"]["workload"]] = bench_line["prefill"]["kernels_ms"]["attention"]
-        off += n_leg
-    for a in bench_line.get("also", []):
-        if "kernels_ms" not in a:                     # a graph replay: launches of its own shape; stop here
-            break
-        legs[a["workload"]] = att[off:off + n_leg]
-        events[a["workload"]] = a["kernels_ms"]["attention"]
-        off += n_leg
+    for e in ([bench_line["prefill"]] if "prefill" in bench_line else []) + bench_line.get("also", []):
+        if "kernels_ms" in e:
+            events[e["workload"]] = e["kernels_ms"]["attention"]
+    legs, off = {}, 0
+    for name, total, timed in bench_line["launch_log"]:
+        ds = att[off:off + total]
+        off += total
+        legs[name] = (len(ds), float(np.mean([x[1] for x in ds[-timed:]])) if ds else float("nan"))
+    assert off == len(att), f"launch log covers {off} of {len(att)} attention dispatches"
     with open(os.path.join(out_dir, "bench_default_kernel_stats.md"), "w") as f:
         f.write("# rocprofv3 kernel statistics of the default bench command\n\n")
         f.write("| kernel | calls | average ns | min ns | max ns | % |\n|---|---|---|---|---|---|\n")
         for r in stats:
             f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                     f"{r['MaxNs']} | {r['Percentage']} |\n")
-        f.write("\nThe attention kernel serves every leg under one name; the per-dispatch trace splits them "
-                "in launch order (first call, warmup, timed steps of each leg):\n\n")
+        f.write("\nThe attention kernel serves every leg under one name; the per-dispatch trace is split by the "
+                "bench's launch log (first call, warmup and timed steps of each leg, in order; a graph leg "
+                "also counts its eager warmup):\n\n")
         f.write("| leg | dispatches | average ns (timed steps) | bench HIP-event ms |\n|---|---|---|---|\n")
-        for wl, ds in legs.items():
-            timed = [x[1] for x in ds[-(steps if wl == bench_line['config']['workload'] else max(5, steps // 2)):]]
-            ev = events[wl]
-            f.write(f"| {wl} | {len(ds)} | {np.mean(timed):.0f} | {ev} |\n")
-        f.write("\nCommands:\n\n```\n" + cmds + "\n```\n")
+        for name, (n, avg) in legs.items():
+            f.write(f"| {name} | {n} | {avg:.0f} | {events.get(name, '(graph replay)')} |\n")
+        f.write("\nCommand:\n\n```\n" + "\n".join(c for c in cmds.splitlines() if "--kernel-trace" in c) +
+                "\n```\n")
     # per-workload counter summaries
     for wl in sorted({x[len("fetch_"):] for x in os.listdir(d)
                       if x.startswith("fetch_") and os.path.isdir(os.path.join(d, x))}):
@@ -371,28 +547,32 @@ def summarize_profiles(d):
         wv = _counter_per_dispatch(os.path.join(d, f"write_{wl}"), "WRITE_SIZE", is_att)
         fb = float(np.median(fv)) * 1024.0 * f_scale
         wb = float(np.median(wv)) * 1024.0 * w_scale
-        timed = None
-        if wl in legs:
-            k = steps if wl == bench_line["config"]["workload"] else max(5, steps // 2)
-            timed = float(np.mean([x[1] for x in legs[wl][-k:]]))
+        timed = next((avg for name, (n, avg) in legs.items() if name.partition("@")[0] == wl), None)
         batch = WORKLOADS[wl]()
         pairs, keys = visible_pairs_and_keys(batch)
         alg = algorithmic_bytes(batch, keys)
+        flops = 4.0 * batch.head_dim * pairs
         summary = {"workload": wl, "kernel": "attention_kernel", "source_sha": source_sha(),
                    "fetch_kib_median": float(np.median(fv)), "write_kib_median": float(np.median(wv)),
                    "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
                    "hbm_bytes_per_launch": int(fb + wb), "algorithmic_bytes": int(alg),
                    "traffic_over_algorithmic": round((fb + wb) / alg, 4),
-                   "avg_ns_rocprof": None if timed is None else round(timed),
-                   "flops": 4.0 * batch.head_dim * pairs}
-        mf = os.path.join(d, f"mfma_{wl}")
-        if os.path.isdir(mf):
-            rows = _csv_rows(mf, "counter_collection.csv")
-            agg = {}
-            for r in rows:
-                if is_att(r["Kernel_Name"]):
-                    agg.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            summary["mfma_counters_median"] = {k: float(np.median(v)) for k, v in agg.items()}
+                   "avg_ns_rocprof": None if timed is None else round(timed), "flops": flops}
+        counters = {}
+        for pas in ("mfma", "pipe"):
+            pd = os.path.join(d, f"{pas}_{wl}")
+            if os.path.isdir(pd):
+                agg = {}
+                for r in _csv_rows(pd, "counter_collection.csv"):
+                    if is_att(r["Kernel_Name"]):
+                        agg.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                med = {k: float(np.median(v)) for k, v in agg.items()}
+                summary[f"{pas}_counters_median"] = med
+                # GRBM_GUI_ACTIVE of each pass goes with that pass's counters
+                counters.update({k: v for k, v in med.items() if k != "GRBM_GUI_ACTIVE" or pas == "mfma"})
+        derived = derive_counters(counters, timed)
+        summary.update(derived)
+        peak = FP8_PEAK_TFLOPS if batch.kind == "e4m3" else BF16_PEAK_TFLOPS
         with open(os.path.join(out_dir, f"attention_kernel_{wl}.md"), "w") as f:
             f.write(f"# attention_kernel on {wl}\n\n")
             f.write(f"HBM traffic per launch: FETCH_SIZE {summary['fetch_kib_median']:.0f} KiB x {f_scale:.3f} + "
@@ -400,7 +580,20 @@ def summarize_profiles(d):
                     f"{summary['hbm_bytes_per_launch'] / 1e6:.1f} MB against {alg / 1e6:.1f} MB algorithmic "
                     f"({summary['traffic_over_algorithmic']:.3f}x).\n\n")
             if timed is not None:
-                f.write(f"Average duration of the timed launches in the kernel trace: {timed / 1e3:.1f} us.\n\n")
+                f.write(f"Average duration of the timed launches in the kernel trace: {timed / 1e3:.1f} us "
+                        f"({alg / timed:.0f} GB/s algorithmic, {flops / timed / 1e3:.1f} TFLOP/s = "
+                        f"{flops / timed / 1e3 / peak:.3f} of the {peak:.0f} TFLOP/s "
+                        f"{'fp8' if batch.kind == 'e4m3' else 'bf16'} peak).\n\n")
+            if "mfma_busy" in derived:
+                f.write(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({N_SIMD} SIMDs x active cycles) = "
+                        f"**{derived['mfma_busy']:.3f}**; active cycles = GRBM_GUI_ACTIVE / {N_XCD} XCDs = "
+                        f"{derived['active_cycles']}, so the clock during the kernel was "
+                        f"{derived.get('clock_ghz')} GHz.\n\n")
+            if "valu_active" in derived:
+                f.write(f"VALU active (SQ_ACTIVE_INST_VALU / ({N_CU} CUs x active cycles), rocprof's VALU "
+                        f"utilisation formula) = {derived['valu_active']:.3f}; LDS active (SQ_LDS_IDX_ACTIVE / "
+                        f"(CUs x cycles)) = {derived.get('lds_idx_active')}; bank conflicts per conflict-free "
+                        f"LDS cycle = {derived.get('lds_bank_conflict_ratio')}.\n\n")
             mine = "\n".join(c for c in cmds.splitlines()
                              if f" {wl} " in c + " " or "--copy-calibration" in c or "--kernel-trace" in c)
             f.write("```json\n" + json.dumps(summary, indent=1) + "\n```\n\nCommands (the copy runs calibrate "
@@ -411,7 +604,7 @@ def summarize_profiles(d):
 
 def profile_leg(name, steps, warmup):
     """One workload only (for counter runs): prints its timing as JSON."""
-    batch, by, flops, ms, kms = leg(name, steps, warmup)
+    batch, by, flops, ms, kms, flushed = leg(name, steps, warmup)
     print(json.dumps({"workload": name, "ms_per_step": ms, "kernels_ms": kms}), flush=True)
 
 
@@ -423,7 +616,8 @@ def main():
     ap.add_argument("--workload", default="splitk_decode_q1_NHD", choices=sorted(WORKLOADS))
     ap.add_argument("--prefill-workload", default="prefill_bf16_dense", choices=sorted(WORKLOADS) + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", default="splitk_decode_q1_HND,splitk_decode_fp8_q1_NHD",
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the headline step")
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
                     help="comma-separated extra workloads to time (reported under 'also'); '' for none")
     ap.add_argument("--profile-leg", default=None, choices=sorted(WORKLOADS),
                     help="time only this workload (for rocprofv3 counter runs)")
@@ -448,10 +642,11 @@ def main():
         profile_leg(args.profile_leg, args.steps, args.warmup)
         return
 
-    batch, by, flops, ms, kms = leg(args.workload, args.steps, args.warmup)
+    batch, by, flops, ms, kms, flushed = leg(args.workload, args.steps, args.warmup)
     gbs = by / (ms * 1e-3) / 1e9
-    att_gbs = by / (kms["attention"] * 1e-3) / 1e9
     dtype = {"f32": "f32", "bf16": "bf16", "e4m3": "fp8"}[batch.kind]
+    roof = roofline_of(args.workload, batch, by, flops, kms["attention"])
+    roof["kernel"] = f"attention_kernel<{ {'f32': 0, 'bf16': 1, 'e4m3': 2}[batch.kind] },{batch.head_dim}>"
     result = {
         "metric": "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), 8B-shape bf16",
         "value": round(gbs, 2),
@@ -470,37 +665,47 @@ def main():
                    "head_dim": batch.head_dim, "page_size": batch.page_size,
                    "kv_layout": batch.kv_layout, "total_q": batch.total_q,
                    "total_keys": int(batch.seq_lens.sum()), "algorithmic_bytes": by},
-        "roofline": {"bound": "hbm", "achieved": round(att_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload),
-                     "kernel": f"attention_kernel<{ {'f32': 0, 'bf16': 1, 'e4m3': 2}[batch.kind] },{batch.head_dim}>"},
+        "roofline": roof,
         "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
+        "flushed": flushed,
     }
+    if not args.no_graph:
+        gms, _, _ = time_workload(batch, args.steps, args.warmup, split="dynamic+graph",
+                                  leg_name=args.workload + "+graph")
+        result["graph_replay"] = {"ms_per_step": round(gms, 5), "gbs_step": round(by / (gms * 1e-3) / 1e9, 1)}
+        log(f"{args.workload} replayed from a HIP graph: {gms:.4f} ms/step")
+    head_batch, head_by = batch, by
+    legs = {}
     if args.prefill_workload != "none":
-        pb, pby, pfl, pms, pkms = leg(args.prefill_workload, max(5, args.steps // 2), args.warmup)
-        peak = FP8_PEAK_TFLOPS if pb.kind == "e4m3" else BF16_PEAK_TFLOPS
-        tf = pfl / (pkms["attention"] * 1e-3) / 1e12
-        result["prefill"] = {"workload": args.prefill_workload, "ms_per_step": round(pms, 5),
-                             "tflops_step": round(pfl / (pms * 1e-3) / 1e12, 2),
-                             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
-                                          "unit": "TFLOP/s", "frac": round(tf / peak, 4),
-                                          "traffic": traffic_for(args.prefill_workload)},
-                             "kernels_ms": {k: round(v, 5) for k, v in pkms.items()}}
+        r = leg(args.prefill_workload, max(5, args.steps // 2), args.warmup)
+        pb, pfl, pms = r[0], r[2], r[3]
+        e = leg_entry(args.prefill_workload, *r)
+        e["tflops_step"] = round(pfl / (pms * 1e-3) / 1e12, 2)
+        result["prefill"] = e
+        legs[args.prefill_workload] = e
         del pb
     also = []
     for name in [x for x in args.extra.split(",") if x]:
-        eb, eby, efl, ems, ekms = leg(name, max(5, args.steps // 2), args.warmup)
-        entry = {"workload": name, "ms_per_step": round(ems, 5), "gbs_step": round(eby / (ems * 1e-3) / 1e9, 1)}
-        if ekms["attention"] == ekms["attention"]:          # per-kernel times exist (not a graph replay)
-            entry.update({"tflops_attention": round(efl / (ekms["attention"] * 1e-3) / 1e12, 2),
-                          "gbs_attention": round(eby / (ekms["attention"] * 1e-3) / 1e9, 1),
-                          "kernels_ms": {k: round(v, 5) for k, v in ekms.items()}})
-        also.append(entry)
-        del eb
+        r = leg(name, max(5, args.steps // 2), args.warmup)
+        e = leg_entry(name, *r)
+        also.append(e)
+        legs[name] = e
+        del r
+    # block-sparse prefill against its own dense run (same quantisation)
+    for m in [x for x in legs if x.endswith("_mask")]:
+        dense = m[:-len("_mask")] + "_dense"
+        if dense in legs and "kernels_ms" in legs[m] and "kernels_ms" in legs[dense]:
+            legs[m]["speedup_vs_dense"] = round(legs[dense]["kernels_ms"]["attention"] /
+                                                legs[m]["kernels_ms"]["attention"], 3)
     if also:
         result["also"] = also
+    result["stream_bandwidth"] = stream_bandwidth()
+    result["launch_log"] = LAUNCH_LOG
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(batch)
+        result["cpu_baseline"] = cpu_baseline(head_batch, head_by)
+        if args.prefill_workload != "none":
+            result["cpu_baseline"]["prefill"] = cpu_baseline_prefill(WORKLOADS[args.prefill_workload]())
     print(json.dumps(result), flush=True)
 
 
