@@ -71,19 +71,23 @@ struct Cfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// bf16, d = 128, one page per tile (the direct path): the two V stages are LDS
-// arrays of their own (vstage), the rest stays in the dynamic block.  The
-// compiler then knows that a DMA into one V stage cannot touch the transpose
-// reads of the other and issues those reads without waiting for every DMA in
-// flight.  Small ranges keep four of their eight stash pieces in the V stages.
+// bf16 or fp8, d = 128, one page per tile (the direct paths): the two V stages
+// (bf16, row-major) are LDS arrays of their own (vstage), the rest stays in
+// the dynamic block.  The compiler then knows that a DMA into one V stage
+// cannot touch the transpose reads of the other and issues those reads
+// without waiting for every DMA in flight.  fp8 V lands first in an 8 KiB
+// staging block after the two K stages and is widened into the V stage.
+// Small ranges keep four of their eight stash pieces in the V stages.
 constexpr int kVStageBytes = 16384;
+constexpr int kV8Bytes = 64 * 128;      // one fp8 V tile (d = 128)
 template <int KIND, int D, bool FAST>
 struct Lds {
   using C = Cfg<KIND, D>;
-  static constexpr bool SPLIT_V = KIND == KIND_BF16 && D == 128 && FAST;
+  static constexpr bool SPLIT_V = (KIND == KIND_BF16 || KIND == KIND_F8) && D == 128 && FAST;
   static constexpr int STASH_PIECES_DYN = SPLIT_V ? kWaves : 2 * kWaves;      // acc pieces in the dynamic block
   static constexpr int STASH_DYN = (2 * 2 * kWaves * 16 + STASH_PIECES_DYN * 16 * D) * 4 + 2 * kWaves * 4;
-  static constexpr int BODY = SPLIT_V ? (2 * C::K_TILE > C::QOFF + C::QBYTES ? 2 * C::K_TILE : C::QOFF + C::QBYTES)
+  static constexpr int KV_DYN = 2 * C::K_TILE + (KIND == KIND_F8 ? kV8Bytes : 0);   // K stages (+ fp8 V staging)
+  static constexpr int BODY = SPLIT_V ? (KV_DYN > C::QOFF + C::QBYTES ? KV_DYN : C::QOFF + C::QBYTES)
                                       : C::BODY0;
   static constexpr int DYN = (BODY > STASH_DYN ? BODY : STASH_DYN) + kMaskListCap * 2;
   static constexpr int TOTAL = DYN + (SPLIT_V ? 2 * kVStageBytes : 0);
@@ -1600,6 +1604,7 @@ struct DirectStage {
   int k_row0, v_row0;         // row of load i = 0 (K: + 16 i, V: + 16 i)
   uint32_t k_lane, v_lane;    // byte offsets of the lane's rows for load i = 0
   uint32_t k8_lane;           // fp8 K (see issue_k8): row m, byte 16 hh of a 64-byte chunk
+  uint32_t v8_lane;           // fp8 V (see issue_v8): row lane / 8, bytes 16 (lane % 8) ..
 
   // (re)point at sequence s.b, kv head s.g; the page window survives while the
   // sequence stays the same
@@ -1632,6 +1637,7 @@ struct DirectStage {
     k_lane = (uint32_t)k_row0 * kss + k_col;
     v_lane = (uint32_t)v_row0 * vss + v_col;
     k8_lane = (uint32_t)m * kss + 16u * hh;
+    v8_lane = (uint32_t)(lane >> 3) * vss + 16u * (lane & 7);
   }
 
   __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
@@ -1661,6 +1667,7 @@ struct DirectStage {
   const char* pk_b;
   const char* pv_b;
   int pnvalid;
+  int ppage;                  // physical page of the prepared tile
   // The addresses of one tile's DMAs; issue(i) then starts DMA i of 8 (K rows
   // for i < 4, V rows after).  A DMA holds its wave until the address unit
   // takes it, so the tile loop spreads the eight over its QK MFMAs.
@@ -1671,6 +1678,7 @@ struct DirectStage {
     pk_b = wave_uniform(kbase + page * ksp + slot * kss);
     pv_b = wave_uniform(vbase + page * vsp + slot * vss);
     pnvalid = min(kUnitKeys, s.ctx - J0);
+    ppage = page;
   }
   // The tile lies in one page, so rows past the sequence end are still cache
   // memory: they are read as they are (their scores are masked by select)
@@ -1683,6 +1691,42 @@ struct DirectStage {
   __device__ __forceinline__ void issue_k8(int c, char* kbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     gload16_lds(wave_uniform(pk_b + (uint32_t)(16 * wave) * kss + 64u * c), kbuf + 1024 * (2 * wave + c), k8_lane, 0u);
+  }
+  // fp8, d = 128: wave w's V rows 16 w + 8 i + lane / 8 (i = 0, 1), 128 bytes
+  // each, lane-linearly into the staging block at v8buf + 1 KiB (2 w + i).
+  // Only wave w reads them back (widen_v8), so the wave's own wait orders
+  // them; the block needs no second buffer.
+  __device__ __forceinline__ void issue_v8(int i, char* v8buf) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    gload16_lds(wave_uniform(pv_b + (uint32_t)(16 * wave + 8 * i) * vss), v8buf + 1024 * (2 * wave + i), v8_lane, 0u);
+  }
+  // After this wave's V DMAs have landed (vmcnt): its 16 rows of fp8 V to
+  // bf16 (exact: every E4M3 value is a bf16), written row-major into the V
+  // stage with the bf16 direct path's swizzle (16-byte chunk q of row r in
+  // slot q ^ 2 (r % 8)).  Rows past the sequence end (the last tile only) are
+  // written as zeros, so no garbage (NaN included) reaches P V.
+  __device__ __forceinline__ void widen_v8(const char* v8buf, char* vbuf) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * wave + 8 * i + (lane >> 3), q = lane & 7;    // fp8 bytes 16 q .. 16 q + 15 of row r
+      u32x4 raw = *reinterpret_cast<const u32x4*>(v8buf + 1024 * (2 * wave + i) + 16 * lane);
+      if (pnvalid < kUnitKeys && r >= pnvalid) raw = u32x4{0, 0, 0, 0};
+      u32x4 lo, hi;                                                  // bf16 dims 16 q .. + 7, 16 q + 8 .. + 15
+      lo[0] = f8x2_to_bf16x2(raw[0]);
+      lo[1] = f8x2_to_bf16x2<true>(raw[0]);
+      lo[2] = f8x2_to_bf16x2(raw[1]);
+      lo[3] = f8x2_to_bf16x2<true>(raw[1]);
+      hi[0] = f8x2_to_bf16x2(raw[2]);
+      hi[1] = f8x2_to_bf16x2<true>(raw[2]);
+      hi[2] = f8x2_to_bf16x2(raw[3]);
+      hi[3] = f8x2_to_bf16x2<true>(raw[3]);
+      char* row = vbuf + 256 * r;
+      const int sw = 2 * (r & 7);
+      *reinterpret_cast<u32x4*>(row + 16 * ((2 * q) ^ sw)) = lo;
+      *reinterpret_cast<u32x4*>(row + 16 * ((2 * q + 1) ^ sw)) = hi;
+    }
   }
   __device__ __forceinline__ void issue(int i, char* kbuf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1735,9 +1779,14 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   constexpr int MD = C::MD;
   constexpr int NB = 2;
   constexpr bool DIRECT = KIND == KIND_BF16 && D == 128 && FAST;
-  // fp8, d = 128, one page per tile: K straight to LDS (issue_k8), V staged
-  // through registers (widened to bf16 there); Q then takes K's chunk order
+  // fp8, d = 128, one page per tile: K straight to LDS in the 16x16x128
+  // operand order (issue_k8; Q takes K's chunk order); V straight to an LDS
+  // staging block (issue_v8), each wave widening its own rows to bf16 into the
+  // V stage (widen_v8), so PV reads bf16 V^T operands as the bf16 path does
   constexpr bool DKF8 = KIND == KIND_F8 && D == 128 && FAST;
+  // PV operands by transpose reads from a row-major bf16 V stage
+  constexpr bool TRV = DIRECT || DKF8;
+  char* const v8buf = smem + 2 * C::K_TILE;         // DKF8: fp8 V staging (single)
   // Row sums of P stay on the VALU in fp32: an MFMA sum of the bf16 P operand
   // carries its rounding (up to 2^-9 on the largest term, which under the lazy
   // rescale is no longer exactly 1) straight into the LSE.
@@ -1802,6 +1851,14 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   Stage<KIND, D, FAST> stg;
   stg.ksc = stg.vsc = 1.f;
   float cur_ksc = 1.f, cur_vsc = 1.f;              // scales of the tile in the current stage
+  // fp8: a V scale per (page, kv head) goes into P tile by tile; the one V
+  // scale of a tensor multiplies O once, in the epilogue
+  bool v_per_tile = false;
+  float v_out = 1.f;
+  if constexpr (DKF8) {
+    v_per_tile = held((p.scale_mode & 3) == 2 ? 1 : 0) != 0;
+    v_out = v_per_tile ? 1.f : p.v_scale[0];
+  }
   if constexpr (FAST) ds.init<C::ELT>(p, s);       // keeps its page window while the sequence stays
 
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
@@ -1818,11 +1875,11 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       ds.prep(p, s, tile_of(c0));
       ds.issue_k8(0, smem);
       ds.issue_k8(1, smem);
-      stg.template load<false>(p, s, tile_of(c0), ds.page_of_tile(p, tile_of(c0) * kUnitKeys));
-      stg.template store<false>(smem, smem + C::K_TILE);
+      ds.issue_v8(0, v8buf);
+      ds.issue_v8(1, v8buf);
+      cur_ksc = kscale_at_page<KIND>(p, s, ds.ppage, &cur_vsc);
       wait_vmem();
-      cur_ksc = stg.ksc;
-      cur_vsc = stg.vsc;
+      ds.widen_v8(v8buf, vstage<true>(0));
     } else {
       stg.load(p, s, tile_of(c0), FAST ? ds.page_of_tile(p, tile_of(c0) * kUnitKeys) : -1);
       stg.store(smem, smem + C::K_TILE);
@@ -1834,13 +1891,23 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     // LDS address is a lane register plus an immediate offset
     auto step = [&](int u, auto buf_c) {
       constexpr int buf = decltype(buf_c)::value;
-      char* kbuf = DIRECT ? smem + buf * C::K_TILE : smem + buf * C::STAGE;
+      char* kbuf = TRV ? smem + buf * C::K_TILE : smem + buf * C::STAGE;
       char* vbuf = kbuf + C::K_TILE;
       const bool more = u + 1 < c0 + cn;
       char* nkb = smem + (buf ^ 1) * C::K_TILE;
-      char* nkb_stage = smem + (buf ^ 1) * C::STAGE;
       char* nvb = nullptr;
-      if constexpr (DIRECT) {
+      float nksc = 1.f, nvsc = 1.f;                    // DKF8: scales of the next tile
+      if constexpr (DKF8) {
+        // the next tile's K and V go out before the QK MFMAs (a chunk's last
+        // step re-loads its own tile into the idle stage, as the bf16 path)
+        nvb = vstage<true>(buf ^ 1);
+        ds.prep(p, s, tile_of(more ? u + 1 : u));
+        ds.issue_k8(0, nkb);
+        ds.issue_k8(1, nkb);
+        ds.issue_v8(0, v8buf);
+        ds.issue_v8(1, v8buf);
+        nksc = kscale_at_page<KIND>(p, s, ds.ppage, &nvsc);
+      } else if constexpr (DIRECT) {
         // the next tile's DMAs go out between the QK MFMAs below (the last
         // step of a chunk re-loads its own tile into the idle stage)
         nvb = vstage<true>(buf ^ 1);
@@ -1850,15 +1917,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           for (int i = 0; i < 8; ++i) ds.issue(i, nkb, nvb);
         }
       } else if (more) {
-        if constexpr (DKF8) {
-          // (issued here rather than spread over the QK MFMAs: measured faster)
-          ds.prep(p, s, tile_of(u + 1));
-          ds.issue_k8(0, nkb_stage);
-          ds.issue_k8(1, nkb_stage);
-          stg.template load<false>(p, s, tile_of(u + 1), ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys));
-        } else {
-          stg.load(p, s, tile_of(u + 1), FAST ? ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys) : -1);
-        }
+        stg.load(p, s, tile_of(u + 1), FAST ? ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys) : -1);
       }
       __builtin_amdgcn_sched_barrier(0);
       const int tile = tile_of(u);
@@ -1993,17 +2052,26 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
                   for (int nb = 0; nb < NB; ++nb)
                     st.acc[nb][4 * gd + i] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], sc[nb][mb][j], st.acc[nb][4 * gd + i], 0, 0, 0);
               }
-        } else if constexpr (DIRECT) {
+        } else if constexpr (TRV) {
           // V^T operands by transpose reads, VDEP operands ahead of their MFMAs
           constexpr int NV = 2 * MD, VDEP = 8;
           auto vread = [&](int i) -> bf16x8 {
             return v_operand_tr(vstage<true>(buf), trx[i % MD], (uint32_t)((i / MD) * 8192));
           };
           bf16x8 pb[2][NB];
+          // fp8 with one V scale for the tensor: applied to O in the epilogue,
+          // not to every P; a V scale per (page, head) changes per tile
+          if (KIND != KIND_F8 || v_per_tile) {
 #pragma unroll
-          for (int ks2 = 0; ks2 < 2; ++ks2)
+            for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) pb[ks2][nb] = p_operand(sc[nb], ks2, vsc);
+              for (int nb = 0; nb < NB; ++nb) pb[ks2][nb] = p_operand(sc[nb], ks2, vsc);
+          } else {
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) pb[ks2][nb] = p_operand(sc[nb], ks2, 1.f);
+          }
           bf16x8 vr[VDEP];
 #pragma unroll
           for (int i = 0; i < VDEP; ++i) vr[i] = vread(i);
@@ -2040,10 +2108,14 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       if constexpr (DIRECT) {
         wait_vmem();
         ds.zero_tail(nvb);
+      } else if constexpr (DKF8) {
+        wait_vmem();                                     // this wave's K and V DMAs have landed
+        ds.widen_v8(v8buf, nvb);
+        cur_ksc = nksc;
+        cur_vsc = nvsc;
       } else if (more) {
         char* nk = smem + (buf ^ 1) * C::STAGE;
-        stg.template store<!DKF8>(nk, nk + C::K_TILE);
-        if constexpr (DKF8) wait_vmem();                 // this wave's K DMAs have landed
+        stg.store(nk, nk + C::K_TILE);
         cur_ksc = stg.ksc;
         cur_vsc = stg.vsc;
       }
@@ -2061,9 +2133,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     const float l = MSUM ? st.lacc[nb][0] : row_sum4(st.lsum[nb]);
     if (!rok[nb]) continue;
     const bool empty = !(l > 0.f);
-    const float inv = empty ? 0.f : 1.f / l;
+    const float inv = empty ? 0.f : (DKF8 && !v_per_tile ? v_out : 1.f) / l;
     const float lse = empty ? kNegInf : (st.m2[nb] + log2f(l)) * kLn2;
-    write_row<KIND, D, DIRECT>(p, x, rowi[nb], h, st.acc[nb], inv, lse, final_out, slot);
+    write_row<KIND, D, TRV>(p, x, rowi[nb], h, st.acc[nb], inv, lse, final_out, slot);
   }
 }
 
