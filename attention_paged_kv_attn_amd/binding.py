@@ -49,7 +49,8 @@ class pa_params(ctypes.Structure):
         (n, ctypes.c_int32) for n in (
             "causal", "window", "window_expand_to_chunk", "landmark_chunk", "block_mask_tile",
             "num_workers", "split_min_units", "force_split_units", "max_partial_slots", "flags",
-            "split_mode", "static_splits", "max_q_len", "min_q_len", "pair_weight", "fused_combine")]
+            "split_mode", "static_splits", "max_q_len", "min_q_len", "pair_weight", "fused_combine",
+            "qblock_per_kv_head")]
 
 
 class pa_workspace_layout(ctypes.Structure):
@@ -57,7 +58,7 @@ class pa_workspace_layout(ctypes.Structure):
         "header", "seq_qb_base", "qb_desc", "unit_prefix", "n_splits", "slot_base", "combine_list",
         "done", "partial_lse", "partial_o", "total")] + [
         ("n_qb_max", ctypes.c_int32), ("max_slots", ctypes.c_int32), ("num_workers", ctypes.c_int32),
-        ("slot_rows", ctypes.c_int32)]
+        ("slot_rows", ctypes.c_int32), ("qblock_heads", ctypes.c_int32)]
 
 
 class pa_device_info(ctypes.Structure):
@@ -152,7 +153,7 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
                 window=0, window_expand_to_chunk=True, landmark_chunk=0, block_mask_tile=128,
                 num_workers=0, split_min_units=0, force_split_units=0, max_partial_slots=0,
                 split_mode=PA_SPLIT_DYNAMIC, static_splits=0, max_q_len=0, min_q_len=0, pair_weight=0,
-                fused_combine=0) -> pa_params:
+                fused_combine=0, qblock_per_kv_head=0) -> pa_params:
     p = pa_params()
     p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
     p.page_size, p.num_pages, p.max_pages_per_seq = page_size, num_pages, max_pages_per_seq
@@ -168,6 +169,7 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num
     p.min_q_len = min_q_len
     p.pair_weight = pair_weight
     p.fused_combine = int(fused_combine)
+    p.qblock_per_kv_head = int(qblock_per_kv_head)
     return p
 
 
@@ -248,7 +250,7 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    force_split_units: int = 0, max_partial_slots: int = 0, split: str = "dynamic",
                    static_splits: int = 0, max_q_len: int = 0, min_q_len: int = 0, pair_weight: int = 0,
                    fused_combine: bool = False, workspace: Optional[torch.Tensor] = None, stream=None,
-                   noalloc: bool = False):
+                   noalloc: bool = False, qblock_per_kv_head: bool = False):
     """Run the library on torch tensors; returns (out, lse, workspace).
 
     noalloc: call paged_attn_fwd_noalloc (the library's own scratch array is
@@ -282,7 +284,7 @@ def paged_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                          split_min_units=split_min_units, force_split_units=force_split_units,
                          max_partial_slots=max_partial_slots, max_q_len=max_q_len, min_q_len=min_q_len,
                          pair_weight=pair_weight,
-                         fused_combine=fused_combine)
+                         fused_combine=fused_combine, qblock_per_kv_head=qblock_per_kv_head)
     if split == "auto":
         params.split_mode, params.static_splits = paged_attn_plan_split(params, seq_lens, query_start_loc,
                                                                         block_mask is not None)

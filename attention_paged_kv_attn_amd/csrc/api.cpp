@@ -82,6 +82,7 @@ pa_status check_params(const pa_params* p) {
   if (p->max_q_len > 0 && p->min_q_len > p->max_q_len) return PA_ERR_INVALID_ARG;
   if (p->pair_weight < 0 || p->pair_weight > 99) return PA_ERR_INVALID_ARG;
   if (p->fused_combine != 0 && p->fused_combine != 1) return PA_ERR_INVALID_ARG;
+  if (p->qblock_per_kv_head != 0 && p->qblock_per_kv_head != 1) return PA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || p->softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;   // finite, positive
   return PA_OK;
 }
@@ -96,6 +97,18 @@ int kernel_paths(const pa_params* p) {
     return 1;
   if (p->min_q_len * G > pa::kSmallMaxRows) return 2;
   return 0;
+}
+
+// Sequence Q-blocks (every query head of a sequence in one Q-block, units
+// its (tile, kv head) pairs): a decode-only dynamic call whose kv heads split
+// evenly over the four waves of a workgroup with each wave's query rows
+// (hpw = Hkv / 4 heads x G x q_len) in one 16-row block.  A call with a block
+// mask uses one Q-block per kv head instead (fwd_impl).
+bool sequence_qblocks(const pa_params* p) {
+  if (kernel_paths(p) != 1 || p->split_mode != PA_SPLIT_DYNAMIC || p->qblock_per_kv_head) return false;
+  const int64_t G = p->num_q_heads / p->num_kv_heads;
+  return p->num_kv_heads % 4 == 0 && p->max_q_len > 0 &&
+         int64_t(p->max_q_len) * G * (p->num_kv_heads / 4) <= pa::kSmallMaxRows;
 }
 
 pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
@@ -113,7 +126,8 @@ pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   // last); an odd P whose last worker pair is cut unevenly uses P + 1
   const int64_t max_slots = p->max_partial_slots ? p->max_partial_slots : 2 * (int64_t(P) + (P & 1));
   // a partial slot holds the largest Q-block the kernel build can meet
-  const int32_t slot_rows = kernel_paths(p) == 1 ? pa::kSmallMaxRows : pa::kLargeRows;
+  int32_t slot_rows = kernel_paths(p) == 1 ? pa::kSmallMaxRows : pa::kLargeRows;
+  if (sequence_qblocks(p)) slot_rows = std::max(slot_rows, p->max_q_len * p->num_q_heads);
   if (n_qb_max > (1 << 30) || max_slots > (1 << 24)) return PA_ERR_INVALID_ARG;
   std::memset(L, 0, sizeof(*L));
   size_t off = 0;
@@ -132,6 +146,7 @@ pa_status layout_of(const pa_params* p, pa_workspace_layout* L) {
   L->max_slots = int32_t(max_slots);
   L->num_workers = P;
   L->slot_rows = slot_rows;
+  L->qblock_heads = sequence_qblocks(p) ? p->num_q_heads : G;
   return PA_OK;
 }
 
@@ -434,6 +449,9 @@ pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor
   kp.pair_w = P.pair_weight ? P.pair_weight : (paths == 1 ? PA_PAIR_WEIGHT_SMALL : PA_PAIR_WEIGHT_GENERAL);
   kp.fused = P.fused_combine ? 1 : 0;
   kp.slot_rows = L.slot_rows;
+  // with a block mask the units of a Q-block follow the mask per kv head
+  kp.seq_qb = sequence_qblocks(params) && !block_mask ? 1 : 0;
+  kp.qbh = kp.seq_qb ? P.num_q_heads : kp.G;
   char* ws = static_cast<char*>(workspace);
   kp.hdr = reinterpret_cast<int32_t*>(ws + L.header);
   kp.seq_qb_base = reinterpret_cast<int32_t*>(ws + L.seq_qb_base);

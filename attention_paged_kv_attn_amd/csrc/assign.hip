@@ -8,7 +8,8 @@
 // map is integer-only and must equal the CPU specification bit for bit:
 //   Q-blocks in (b, g) order, a large Q-block's token blocks zig-zag
 //   (0, n-1, 1, n-2, ...); n_units = active 64-key tiles; prefix S;
-//   L = force ? force : max(L_min, ceil(U / P)); worker pair k owns
+//   (or one Q-block per sequence, units = its (tile, kv head) pairs, kv head
+//   fastest); L = force ? force : max(L_min, ceil(U / P)); worker pair k owns
 //   [2kL, 2kL + 2L), the first L0 units to worker 2k (L0 from the pair
 //   weight, L0 = L at 50); worker_of(u) as in WorkerMap;
 //   n_splits(q) = 0 | worker_of(S+n-1) - worker_of(S) + 1; combine list = the
@@ -88,8 +89,12 @@ __device__ int assign_sequences(const KParams& p, int* sh, int* err, int* base_l
     int nqb = 0;
     if (b < p.B) {
       const int ql = p.qsl[b + 1] - p.qsl[b];
-      nqb = ql <= 0 ? 0 : (ql * p.G <= kSmallMaxRows ? 1 : (ql + nt_large - 1) / nt_large);
-      nqb *= p.Hkv;
+      if (p.seq_qb) {
+        nqb = ql > 0 ? 1 : 0;                       // one Q-block with every query head
+      } else {
+        nqb = ql <= 0 ? 0 : (ql * p.G <= kSmallMaxRows ? 1 : (ql + nt_large - 1) / nt_large);
+        nqb *= p.Hkv;
+      }
     }
     const int ex = block_exclusive_scan(nqb, &tot, sh);
     if (b < p.B) {
@@ -119,16 +124,20 @@ __device__ __forceinline__ QbTiles assign_descriptor(const KParams& p, int q, co
     if (base[mid] <= q) lo = mid; else hi = mid - 1;
   }
   const int b = lo;
-  const int nt_large = kLargeRows / p.G;
-  const int per_g = (base[b + 1] - base[b]) / p.Hkv;
-  const int rem = q - base[b];
-  const int g = rem / per_g, t = rem % per_g;
   const int q0 = p.qsl[b], ql = p.qsl[b + 1] - q0, ctx = p.seq_lens[b];
-  const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
-  // zig-zag over the token blocks (spreads short and long Q-blocks evenly)
-  const int zi = (t & 1) ? per_g - 1 - (t >> 1) : (t >> 1);
-  const int t0 = zi * ntl;
-  const int nt = min(ntl, ql - t0);
+  int g = 0, t0 = 0, nt = ql;                        // a sequence Q-block: every head, every token
+  if (!p.seq_qb) {
+    const int nt_large = kLargeRows / p.G;
+    const int per_g = (base[b + 1] - base[b]) / p.Hkv;
+    const int rem = q - base[b];
+    g = rem / per_g;
+    const int t = rem % per_g;
+    const int ntl = ql * p.G <= kSmallMaxRows ? ql : nt_large;
+    // zig-zag over the token blocks (spreads short and long Q-blocks evenly)
+    const int zi = (t & 1) ? per_g - 1 - (t >> 1) : (t >> 1);
+    t0 = zi * ntl;
+    nt = min(ntl, ql - t0);
+  }
   reinterpret_cast<int4*>(p.qb_desc)[2 * q] = make_int4(b, g, t0, nt);
   reinterpret_cast<int4*>(p.qb_desc)[2 * q + 1] = make_int4(q0, ql, ctx, 0);   // saves the kernel two dependent loads
   QbTiles r;
@@ -218,7 +227,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(KParams p) {
   // 2. descriptors and unit counts (counts parked at [q + 1])
   for (int q = threadIdx.x; q < n_qb; q += kAssignThreads) {
     const QbTiles r = assign_descriptor(p, q, bl ? bl : p.seq_qb_base);
-    const int n = r.any ? r.t_hi - r.t_lo + 1 : 0;
+    // a sequence Q-block's units are its (tile, kv head) pairs
+    const int n = r.any ? (r.t_hi - r.t_lo + 1) * (p.seq_qb ? p.Hkv : 1) : 0;
     if (pl) pl[q + 1] = n;
     else p.unit_prefix[q + 1] = n;
   }

@@ -4,13 +4,21 @@
 
 namespace pa {
 
+// Items are (Q-block, chunk of CR rows), at most eight chunks per Q-block
+// (the largest the call can have is slot_rows rows): a chunk of 64 threads
+// leaves the workgroup's four thread groups to share its splits, and a wide
+// Q-block (a sequence Q-block with every query head) spreads over
+// workgroups.
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(KParams p) {
   __shared__ MergeState red[256];
+  const int CR = merge_chunk_rows<D>(p);
+  const int chunks = (p.slot_rows + CR - 1) / CR;
   const bool stat = p.static_S > 0;
   // static split: every Q-block is a candidate, its split count recomputed
   const int n_combine = stat ? p.B * p.Hkv : p.hdr[H_NCOMBINE];
-  for (int i = blockIdx.x; i < n_combine; i += gridDim.x) {
+  for (int it = blockIdx.x; it < n_combine * chunks; it += gridDim.x) {
+    const int i = it / chunks, r0 = (it - i * chunks) * CR;
     int q, ns, sb;
     QBlock x;
     if (stat) {
@@ -25,7 +33,8 @@ __global__ __launch_bounds__(256) void combine_kernel(KParams p) {
       ns = p.n_splits[q];
       sb = p.slot_base[q];
     }
-    merge_qblock<D, OUT_F32>(p, x, ns, sb, red);
+    if (r0 >= x.rows) continue;
+    merge_rows<D, OUT_F32>(p, x, ns, sb, r0, min(CR, x.rows - r0), red);
   }
 }
 

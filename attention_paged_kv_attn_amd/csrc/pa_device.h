@@ -58,7 +58,9 @@ struct KParams {
   int32_t min_q_len; // > 0: the caller's bound below every non-zero q_len (checked by Assign)
   int32_t pair_w;    // percent of a worker pair's 2L units given to its first worker
   int32_t fused;     // 1: the last workgroup to finish a split Q-block merges it (no Combine launch)
-  int32_t slot_rows; // rows per partial slot: the kernel build's largest Q-block (16 or 128)
+  int32_t slot_rows; // rows per partial slot: the kernel build's largest Q-block
+  int32_t seq_qb;    // 1: one Q-block per sequence with all its query heads (decode, heads interleaved)
+  int32_t qbh;       // query heads per token in a Q-block's rows: Hq when seq_qb, else G
   // workspace
   int32_t* hdr; int32_t* seq_qb_base; int32_t* qb_desc; int32_t* unit_prefix;
   int32_t* n_splits; int32_t* slot_base; int32_t* combine_list;
@@ -121,7 +123,8 @@ struct WorkerMap {
   __device__ __forceinline__ int size(int w) const { return (w & 1) ? 2 * L - L0 : L0; }
 };
 
-// Decoded Q-block: rows are (token t0 + r / G, head g * G + r % G).
+// Decoded Q-block: rows are (token t0 + r / qbh, head g * G + r % qbh), with
+// qbh = G (one kv head) or Hq (a sequence Q-block, g = 0).
 struct QBlock {
   int b, g, t0, nt, rows, ql, ctx, q0, pos_lo, pos_hi;
 };
@@ -138,7 +141,7 @@ __device__ __forceinline__ QBlock load_qblock(const KParams& p, int q) {
   x.g = dp[1];
   x.t0 = dp[2];
   x.nt = dp[3];
-  x.rows = x.nt * p.G;
+  x.rows = x.nt * p.qbh;
   x.q0 = dp[4];
   x.ql = dp[5];
   x.ctx = dp[6];

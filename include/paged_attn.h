@@ -150,6 +150,15 @@ typedef struct pa_params {
                                    counter in the workspace, partials through device-coherent
                                    accesses), one launch fewer.  Measured slower on MI355X
                                    (the merges land on the kernel's tail), so not the default */
+  int32_t qblock_per_kv_head;   /* 0: the library's choice: a decode-only dynamic call (max_q_len
+                                   set, max_q_len * Hq / Hkv <= 16) with Hkv % 4 == 0 and
+                                   max_q_len * (Hq / Hkv) * (Hkv / 4) <= 16, and no block mask, gets
+                                   one Q-block per sequence holding all its query heads, whose units
+                                   are (64-key tile, kv head) pairs with the kv head fastest: the
+                                   four waves of a workgroup then read the same keys of different
+                                   kv heads together, which an NHD cache (kv heads adjacent in a
+                                   page) serves at a higher rate.  1: always one Q-block per kv
+                                   head. */
 } pa_params;
 
 #define PA_PAIR_WEIGHT_SMALL 60
@@ -194,7 +203,10 @@ typedef struct pa_workspace_layout {
   int32_t max_slots;
   int32_t num_workers;
   int32_t slot_rows;      /* rows per partial slot: 16 when every Q-block is known to be small
-                             (PA_SPLIT_STATIC, or max_q_len * Hq / Hkv <= 16), else 128 */
+                             (PA_SPLIT_STATIC, or max_q_len * Hq / Hkv <= 16), max_q_len * Hq with
+                             sequence Q-blocks, else 128 */
+  int32_t qblock_heads;   /* query heads per token in a Q-block's rows: Hq for sequence Q-blocks
+                             (see pa_params.qblock_per_kv_head), else Hq / Hkv */
 } pa_workspace_layout;
 
 typedef struct pa_device_info {

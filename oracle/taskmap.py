@@ -56,6 +56,17 @@ Specification
   Q-blocks with n_splits >= 2 get partial slots slot_base(q) = running sum of
   n_splits over earlier such Q-blocks (-1 for the others); n_slots = total.
 
+Sequence Q-blocks (heads interleaved)
+-------------------------------------
+* A decode batch may instead be cut into one Q-block per sequence holding all
+  of its query heads: (b, 0, 0, q_len) for every b with q_len > 0, row r =
+  token r // Hq, query head r % Hq.  Its units are the (tile, kv head)
+  pairs, kv head fastest: unit k is tile tile_lo + k // Hkv of kv head
+  k % Hkv, so n = Hkv * (tile_hi - tile_lo + 1) with the tile range above
+  (no block mask).  Everything after the unit counts (prefix, L, workers,
+  splits, slots) is unchanged.  (The four waves of a workgroup then read the
+  same keys of different kv heads at the same time.)
+
 Static split (no task map)
 --------------------------
 * The static variant of the same page's Split-K (a fixed number of splits
@@ -80,14 +91,16 @@ def _window_left(pos, window, expand, chunk):
     return left
 
 
-def q_blocks(seq_lens, query_start_loc, Hq, Hkv):
+def q_blocks(seq_lens, query_start_loc, Hq, Hkv, heads_interleaved=False):
     G = Hq // Hkv
     out = []
     for b in range(len(seq_lens)):
         ql = int(query_start_loc[b + 1]) - int(query_start_loc[b])
         if ql <= 0:
             continue
-        if ql * G <= SMALL_MAX_ROWS:
+        if heads_interleaved:
+            out.append((b, 0, 0, ql))
+        elif ql * G <= SMALL_MAX_ROWS:
             for g in range(Hkv):
                 out.append((b, g, 0, ql))
         else:
@@ -102,7 +115,7 @@ def q_blocks(seq_lens, query_start_loc, Hq, Hkv):
 
 
 def unit_count(desc, seq_lens, query_start_loc, Hq, Hkv, *, causal, window, expand_to_chunk,
-               landmark_chunk, block_mask=None, block_mask_tile=128):
+               landmark_chunk, block_mask=None, block_mask_tile=128, heads_interleaved=False):
     b, g, t0, nt = desc
     G = Hq // Hkv
     ctx = int(seq_lens[b])
@@ -114,6 +127,10 @@ def unit_count(desc, seq_lens, query_start_loc, Hq, Hkv, *, causal, window, expa
     if hi < lo:
         return 0
     t_lo, t_hi = lo // UNIT_KEYS, hi // UNIT_KEYS
+    if heads_interleaved:
+        if block_mask is not None:
+            raise ValueError("sequence Q-blocks take no block mask")
+        return Hkv * (t_hi - t_lo + 1)
     if block_mask is None:
         return t_hi - t_lo + 1
     heads = [0] if block_mask.shape[1] == 1 else list(range(g * G, (g + 1) * G))
@@ -141,13 +158,15 @@ def worker_range(w, L, L0, U):
 
 def build(seq_lens, query_start_loc, *, Hq, Hkv, num_workers, split_min_units=8,
           force_split_units=0, causal=True, window=0, window_expand_to_chunk=True,
-          landmark_chunk=0, block_mask=None, block_mask_tile=128, pair_weight=50):
+          landmark_chunk=0, block_mask=None, block_mask_tile=128, pair_weight=50,
+          heads_interleaved=False):
     seq_lens = [int(x) for x in seq_lens]
     qsl = [int(x) for x in query_start_loc]
-    descs = q_blocks(seq_lens, qsl, Hq, Hkv)
+    descs = q_blocks(seq_lens, qsl, Hq, Hkv, heads_interleaved)
     n = [unit_count(dsc, seq_lens, qsl, Hq, Hkv, causal=causal, window=window,
                     expand_to_chunk=window_expand_to_chunk, landmark_chunk=landmark_chunk,
-                    block_mask=block_mask, block_mask_tile=block_mask_tile) for dsc in descs]
+                    block_mask=block_mask, block_mask_tile=block_mask_tile,
+                    heads_interleaved=heads_interleaved) for dsc in descs]
     prefix = [0]
     for x in n:
         prefix.append(prefix[-1] + x)

@@ -62,13 +62,17 @@ def test_workspace_size_closed_form():
 def test_partial_slots_follow_the_kernel_build():
     """A call whose Q-blocks are all known to be small (max_q_len * G <= 16, or
     a static split) gets 16-row partial slots; otherwise slots hold 128 rows."""
-    for kw, rows in ((dict(max_q_len=4), 16), (dict(max_q_len=5), 128), (dict(min_q_len=32), 128),
-                     (dict(split_mode=B.PA_SPLIT_STATIC, static_splits=2), 16), ({}, 128)):
+    # (Hq 32, Hkv 8: G = 4, two kv heads per wave.)  Sequence Q-blocks hold
+    # max_q_len * Hq rows; they apply while max_q_len * G * Hkv / 4 <= 16
+    for kw, rows, heads in ((dict(max_q_len=4), 16, 4), (dict(max_q_len=1), 32, 32), (dict(max_q_len=2), 64, 32),
+                            (dict(max_q_len=1, qblock_per_kv_head=1), 16, 4), (dict(max_q_len=5), 128, 4),
+                            (dict(min_q_len=32), 128, 4), (dict(split_mode=B.PA_SPLIT_STATIC, static_splits=2), 16, 4),
+                            (dict(max_q_len=1, num_q_heads=12, num_kv_heads=6), 16, 2), ({}, 128, 4)):
         lay = B.paged_attn_workspace_layout(_params(**kw))
-        assert lay.slot_rows == rows, kw
+        assert (lay.slot_rows, lay.qblock_heads) == (rows, heads), kw
         assert lay.partial_o - lay.partial_lse >= lay.max_slots * rows * 4
         assert lay.total - lay.partial_o >= lay.max_slots * rows * 128 * 4
-    small = B.paged_attn_workspace_size(_params(max_q_len=1))
+    small = B.paged_attn_workspace_size(_params(max_q_len=1, qblock_per_kv_head=1))
     assert small < B.paged_attn_workspace_size(_params()) // 4
 
 

@@ -97,19 +97,29 @@ def effective_pair_weight(b, weight=0):
     return B.PA_PAIR_WEIGHT_SMALL if small else B.PA_PAIR_WEIGHT_GENERAL
 
 
-def oracle_taskmap(b, P, force=0, weight=0):
+def sequence_qblocks(b, **kw):
+    """Whether the library cuts a run_batch call on b into one Q-block per
+    sequence (the layout reports the query heads per Q-block)."""
+    if b.block_mask is not None:
+        return False
+    lay = B.paged_attn_workspace_layout(params_of(b, max_q_len=kw.get("max_q_len", b.max_q_len),
+                                                  qblock_per_kv_head=int(kw.get("qblock_per_kv_head", 0))))
+    return lay.qblock_heads != b.num_q_heads // b.num_kv_heads
+
+
+def oracle_taskmap(b, P, force=0, weight=0, **kw):
     return taskmap.build(b.seq_lens.numpy(), b.query_start_loc.numpy(), Hq=b.num_q_heads,
                          Hkv=b.num_kv_heads, num_workers=P, split_min_units=8, force_split_units=force,
                          pair_weight=effective_pair_weight(b, weight),
                          causal=b.causal, window=b.window, window_expand_to_chunk=b.window_expand_to_chunk,
                          landmark_chunk=b.landmark_chunk,
                          block_mask=None if b.block_mask is None else b.block_mask.numpy(),
-                         block_mask_tile=b.block_mask_tile)
+                         block_mask_tile=b.block_mask_tile, heads_interleaved=sequence_qblocks(b, **kw))
 
 
-def slots_for(b, P, force, weight=0):
+def slots_for(b, P, force, weight=0, **kw):
     """Partial slots a forced split needs (the default 2 P covers natural splits)."""
-    return max(1, oracle_taskmap(b, P, force, weight)["n_slots"]) if force else 0
+    return max(1, oracle_taskmap(b, P, force, weight, **kw)["n_slots"]) if force else 0
 
 
 def sample_rows(total_q, k, seed=0, must=()):
@@ -751,3 +761,42 @@ def test_gqa_ratios(G, kind):
         compare(dec, out, lse)
     else:
         assert h[7] == 6                          # PA_DEV_STATIC_ROWS: a Q-block beyond 16 rows
+
+
+
+# Sequence Q-blocks: a decode batch whose kv heads split over the four waves
+# (Hkv % 4 == 0, q_len * G * Hkv / 4 <= 16) gets one Q-block per sequence with
+# every query head; units are (tile, kv head) pairs and each wave owns Hkv / 4
+# kv heads.  Checked against the oracle and against one Q-block per kv head.
+@pytest.mark.parametrize("kind,layout", [("bf16", "NHD"), ("bf16", "HND"), ("e4m3", "NHD"), ("e4m3", "HND")])
+@pytest.mark.parametrize("q_len", [1, [1, 2, 0, 2]])
+def test_sequence_qblocks_decode(kind, layout, q_len):
+    b = W.splitk_decode(q_len=q_len if isinstance(q_len, int) else q_len * 5, batch=20, ctx_lo=40, ctx_hi=5000,
+                        kv_layout=layout, kind=kind, q_gain=4.0)
+    assert sequence_qblocks(b)
+    P = B.paged_attn_device_info(0)["default_workers"]
+    for kw in ({}, {"num_workers": 37}, {"force_split_units": 1}, {"force_split_units": 3, "fused_combine": True}):
+        if "force_split_units" in kw:
+            kw = dict(kw, max_partial_slots=slots_for(b, kw.get("num_workers") or P, kw["force_split_units"]))
+        g, out, lse, ws = gpu_run(b, **kw)
+        check_no_device_error(ws, g)
+        compare(b, out, lse)
+    # the per-kv-head Q-blocks of the same batch agree within the tolerance
+    g, o2, l2, ws2 = gpu_run(b, qblock_per_kv_head=True)
+    check_no_device_error(ws2, g)
+    to, tl = TOL[b.kind]
+    assert (o2.float() - out.float()).abs().max().item() <= to and (l2 - lse).abs().max().item() <= tl
+
+
+def test_sequence_qblocks_window_and_short_sequences():
+    """Windowed decode with landmarks, sequences shorter than a tile and a
+    q_len 0 sequence, under the dynamic split."""
+    rng = np.random.default_rng(31)
+    b = W.build_batch(rng, name="seqqb_window", kind="bf16", Hq=32, Hkv=8, d=128, page_size=64,
+                      ctx=[3, 64, 65, 700, 4100, 90, 1], q_len=[1, 1, 2, 2, 1, 0, 1], window=300,
+                      landmark_chunk=64)
+    assert sequence_qblocks(b)
+    for kw in ({}, {"force_split_units": 2, "max_partial_slots": 4096}):
+        g, out, lse, ws = gpu_run(b, **kw)
+        check_no_device_error(ws, g)
+        compare(b, out, lse)

@@ -214,3 +214,29 @@ def test_static_map_partitions_each_q_block(S, rule):
 def test_static_map_rejects_large_q_blocks():
     with pytest.raises(ValueError):
         taskmap.static_map([100], [0, 5], Hq=32, Hkv=8, S=2)        # 5 tokens x G 4 = 20 rows > 16
+
+
+@pytest.mark.parametrize("P", [7, 64, 512])
+@pytest.mark.parametrize("rule", [dict(causal=True), dict(causal=True, window=300, chunk=64)])
+def test_sequence_q_blocks(P, rule):
+    """One Q-block per sequence with queries, holding every query head; its
+    units are the (visible tile, kv head) pairs, so it counts Hkv times the
+    tiles a brute-force visibility scan finds, and the batch's total work
+    equals that of one Q-block per kv head."""
+    rng = np.random.default_rng(21)
+    ctx = [int(c) for c in W.decode_ctx_lengths(rng, 24, 64, 4000)]
+    ql = [1, 2, 0, 1] * 6
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    kw = dict(causal=rule["causal"], window=rule.get("window", 0), window_expand_to_chunk=True,
+              landmark_chunk=rule.get("chunk", 0))
+    tm = taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=P, heads_interleaved=True, **kw)
+    _check_invariants(tm)
+    assert [tuple(d) for d in tm["desc"]] == [(b, 0, 0, ql[b]) for b in range(len(ctx)) if ql[b]]
+    for desc, n in zip(tm["desc"], tm["n_units"]):
+        b = desc[0]
+        assert n == 8 * _brute_units((b, 0, 0, ql[b]), ctx[b], ql[b], **rule)
+    per_head = taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=P, **kw)
+    assert per_head["U"] == tm["U"] and per_head["n_qb"] == 8 * tm["n_qb"]
+    with pytest.raises(ValueError):
+        taskmap.build(ctx, qsl, Hq=32, Hkv=8, num_workers=P, heads_interleaved=True,
+                      block_mask=np.ones((24, 1, 40, 40), np.uint8), **kw)
