@@ -487,7 +487,8 @@ pa_status fwd_impl(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor
       ++n_events;
     }
   }
-  hipError_t e = launch_all(kp, P, L, kind, paths, stream, timing ? tc.ev : nullptr);
+  // sequence Q-blocks run a kernel build of their own
+  hipError_t e = launch_all(kp, P, L, kind, kp.seq_qb ? 3 : paths, stream, timing ? tc.ev : nullptr);
   if (e != hipSuccess) return fail(e);
   if (timing) {
     std::lock_guard<std::mutex> lk(g_timing_mu);

@@ -1470,6 +1470,9 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
 // (the output, or its rows of the worker's partial slot), so no wave merges
 // with another.
 // ---------------------------------------------------------------------------
+template <int KIND>
+constexpr bool kHeadsHalfStep = true;
+
 template <int KIND, int D, bool FAST>
 __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap wm, int a, int b) {
   const KParams& p = kparams_at(pk);
@@ -1508,12 +1511,13 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
     }
     WaveState<KIND, D, 1> st;
     st.init();
-    for (int k0 = (lo / Hkv) * Hkv; k0 < hi; k0 += Hkv) {
-      const int tile = t_lo + k0 / Hkv;
+    // the page of a tile, from a window of 64 page-table entries held one per
+    // lane (a register read, not a dependent load, for most tiles)
+    auto page_at = [&](int tile) {
       int page = 0;
       if constexpr (FAST) {
         const int idx = (tile * kUnitKeys) >> p.page_shift;
-        if ((unsigned)(idx - pbase) >= 64u) {            // refill the page window (rare)
+        if ((unsigned)(idx - pbase) >= 64u) {            // refill the window (rare)
           pbase = idx;
           int v = s.bt_row[min(idx + lane, p.max_pages - 1)];
           asm volatile("" : "+v"(v));
@@ -1525,25 +1529,80 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
           page = 0;
         }
       }
-      for (int jj = 0; jj < hpw; ++jj) {
-        const int g = wave * hpw + jj, k = k0 + g;
-        if (k < lo || k >= hi) continue;              // uniform: the range may start or end mid-tile
-        s.g = g;
-        Tile<C::ELT, FAST> t;
-        if constexpr (FAST) t.init_at_page(p, s, tile, page);
-        else t.init(p, s, tile);
-        // lane offsets from an opaque copy of the thread id (rebuilt per tile, not spilled)
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        SmallRegs<KIND, D> r;
-        small_load_k<KIND, D, FAST>(p, s, t, r, tid & 15, (tid >> 4) & 3);
-        small_load_v<KIND, D, FAST>(p, s, t, r, tid & 15, (tid >> 4) & 3);
-        rm.bit = row_ok && rkv == g;                   // only this kv head's rows see the tile
+      return page;
+    };
+    // the wave's units of q in order: (k0 = tile * Hkv, j) is kv head
+    // w hpw + j of that tile, a unit of this worker when it lies in [lo, hi)
+    auto valid = [&](int kk0, int j) {
+      const int k = kk0 + wave * hpw + j;
+      return k >= lo && k < hi;
+    };
+    auto advance = [&](int& kk0, int& j) {
+      do {
+        if (++j == hpw) {
+          j = 0;
+          kk0 += Hkv;
+        }
+      } while (kk0 < hi && !valid(kk0, j));
+    };
+    auto prepare = [&](Tile<C::ELT, FAST>& t, SeqCtx& sx, int kk0, int j) {
+      const int tile = t_lo + kk0 / Hkv;
+      sx.g = wave * hpw + j;
+      if constexpr (FAST) t.init_at_page(p, sx, tile, page_at(tile));
+      else t.init(p, sx, tile);
+    };
+    int k0 = (lo / Hkv) * Hkv, jj = 0;
+    if (!valid(k0, jj)) advance(k0, jj);
+    Tile<C::ELT, FAST> tc, tn;
+    SeqCtx sc_ = s, sn = s;
+    SmallRegs<KIND, D> r;
+    // lane offsets from an opaque copy of the thread id (rebuilt per tile, not spilled)
+    auto lane_n = [&]() { int tid = threadIdx.x; asm volatile("" : "+v"(tid)); return tid; };
+    if constexpr (!kHeadsHalfStep<KIND>) {
+      // one tile in flight per wave: the second wave on each SIMD computes
+      // while this one waits
+      for (; k0 < hi; advance(k0, jj)) {
+        prepare(tc, sc_, k0, jj);
+        const int tid = lane_n();
+        small_load_k<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
+        small_load_v<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
+        rm.bit = row_ok && rkv == sc_.g;                 // only this kv head's rows see the tile
         f32x4 sc[4];
-        const float vsc = small_scores<KIND, D, FAST>(p, s, x, t, r, QFromRegs<KIND, D>{qB}, rm, 0, pos_min,
+        const float vsc = small_scores<KIND, D, FAST>(p, sc_, x, tc, r, QFromRegs<KIND, D>{qB}, rm, 0, pos_min,
                                                        left_max, st, lane, sc, mixed);
         small_pv<KIND, D>(r, sc, vsc, st);
       }
+    } else if (k0 < hi) {
+      prepare(tc, sc_, k0, jj);
+      const int tid = lane_n();
+      small_load_k<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
+      small_load_v<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
+    }
+    // half a tile ahead: the next unit's K goes out once this unit's QK has
+    // read K, its V once this unit's PV has read V, so a wave keeps loads in
+    // flight through its own compute without a second tile of registers
+    while (kHeadsHalfStep<KIND> && k0 < hi) {
+      int nk0 = k0, nj = jj;
+      advance(nk0, nj);
+      const bool more = nk0 < hi;
+      rm.bit = row_ok && rkv == sc_.g;                   // only this kv head's rows see the tile
+      f32x4 sc[4];
+      const float vsc = small_scores<KIND, D, FAST>(p, sc_, x, tc, r, QFromRegs<KIND, D>{qB}, rm, 0, pos_min,
+                                                     left_max, st, lane, sc, mixed);
+      if (more) {
+        prepare(tn, sn, nk0, nj);
+        const int tid = lane_n();
+        small_load_k<KIND, D, FAST>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
+      }
+      small_pv<KIND, D>(r, sc, vsc, st);
+      if (more) {
+        const int tid = lane_n();
+        small_load_v<KIND, D, FAST>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
+      }
+      tc = tn;
+      sc_ = sn;
+      k0 = nk0;
+      jj = nj;
     }
     const float l = row_sum4(st.lsum[0]);
     const bool final_out = p.n_splits[q] == 1;
@@ -2290,11 +2349,12 @@ __device__ __forceinline__ void static_items(uint64_t pk) {
 // the same.  The small-only kernel reports a large Q-block (E_QLEN_HINT) and
 // skips it; the large-only kernel runs the few-row tail Q-blocks of long
 // sequences on the 128-row path (Assign rejects short sequences under it).
-constexpr int kPathsAll = 0, kPathsSmall = 1, kPathsLarge = 2;
+// kPathsHeads is the kernel for sequence Q-blocks (heads_range only).
+constexpr int kPathsAll = 0, kPathsSmall = 1, kPathsLarge = 2, kPathsHeads = 3;
 
 template <int KIND, int D, bool FAST, int PATHS>
 __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention_kernel(KParams) {
-  constexpr bool SMALL = PATHS == kPathsSmall, LARGE = PATHS == kPathsLarge;
+  constexpr bool SMALL = PATHS == kPathsSmall, LARGE = PATHS == kPathsLarge, HEADS = PATHS == kPathsHeads;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t pk = kparams_addr();
   const KParams& p = kparams_at(pk);
@@ -2325,7 +2385,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   // first (weighted) run.  The general kernel keeps workers r and r + grid / 16
   // on one unit (measured faster for prefill and sliding-window batches).
   int rank = blockIdx.x;
-  if (SMALL && (gridDim.x & 15) == 0) {
+  if ((SMALL || HEADS) && (gridDim.x & 15) == 0) {
     const int half = gridDim.x >> 1, b = blockIdx.x % half;
     rank = 2 * ((b & 7) * (half >> 3) + (b >> 3)) + (blockIdx.x >= half ? 1 : 0);
   } else if (gridDim.x % 8 == 0) {
@@ -2339,11 +2399,9 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
   for (int vw = rank; vw < n_workers; vw += gridDim.x) {
     int a = wm.start(vw);
     const int b_end = min(a + wm.size(vw), U);
-    if constexpr (SMALL) {
-      if (p.seq_qb) {                                  // sequence Q-blocks: every wave writes its own rows
-        heads_range<KIND, D, FAST>(pk, vw, wm, a, b_end);
-        continue;
-      }
+    if constexpr (HEADS) {                              // sequence Q-blocks: every wave writes its own rows
+      heads_range<KIND, D, FAST>(pk, vw, wm, a, b_end);
+      continue;
     }
     int q = find_qblock(p, 0, n_qb - 1, a, threadIdx.x & 63);
     while (a < b_end && q < n_qb) {
@@ -2426,6 +2484,7 @@ static hipError_t launch_attention_s(const KParams& p, int kind, int grid, hipSt
 }
 
 hipError_t launch_attention(const KParams& p, int kind, int grid, int paths, hipStream_t stream) {
+  if (paths == kPathsHeads) return launch_attention_s<kPathsHeads>(p, kind, grid, stream);
   if (paths == kPathsSmall) return launch_attention_s<kPathsSmall>(p, kind, grid, stream);
   if (paths == kPathsLarge) return launch_attention_s<kPathsLarge>(p, kind, grid, stream);
   return launch_attention_s<kPathsAll>(p, kind, grid, stream);
