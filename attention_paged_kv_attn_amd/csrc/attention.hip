@@ -258,11 +258,19 @@ __device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_
 __device__ __forceinline__ unsigned gload4(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL unsigned*)(base + soff + voff);
 }
-// Direct HBM -> LDS: every lane fetches 16 B at base + soff + voff; the wave
-// writes them lane-linearly (1 KiB) at the wave-uniform LDS address `dst`.
-__device__ __forceinline__ void gload16_lds(const char* base, char* dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_global_load_lds((const PA_GLOBAL void*)(base + soff + voff),
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+// Direct HBM -> LDS through a buffer resource: every lane fetches 16 B at
+// rsrc.base + soff + voff; the wave writes them lane-linearly (1 KiB) at the
+// wave-uniform LDS address `dst`.  The base lives in scalar registers (a
+// resource per tile) and the lane offset in a VGPR fixed for a segment, so a
+// DMA costs no vector address arithmetic (a 64-bit global address per lane
+// took two VALU instructions and read-backs per DMA).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
+  // raw buffer: no stride, a range past any offset used (offsets stay inside
+  // one page of the cache), the gfx9 default data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t rsrc, char* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
 // Rows of one 64-key tile.  FAST (page_size >= 64): the tile lies in one page,
@@ -1828,6 +1836,7 @@ struct DirectStage {
   // last key (finite values; their scores are masked).
   const char* pk_b;
   const char* pv_b;
+  __amdgpu_buffer_rsrc_t krs, vrs;  // the prepared tile's K and V rows (buffer resources)
   int pnvalid;
   int ppage;                  // physical page of the prepared tile
   // The addresses of one tile's DMAs; issue(i) then starts DMA i of 8 (K rows
@@ -1837,8 +1846,14 @@ struct DirectStage {
     const int J0 = tile * kUnitKeys;
     const int page = page_of_tile(p, J0);
     const uint32_t slot = (uint32_t)(J0 & page_mask);
-    pk_b = wave_uniform(kbase + page * ksp + slot * kss);
-    pv_b = wave_uniform(vbase + page * vsp + slot * vss);
+    // scalar arithmetic throughout (a stride left in a VGPR would put the
+    // products on the VALU and read them back)
+    const uint32_t kss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)kss);
+    const uint32_t vss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)vss);
+    pk_b = wave_uniform(wave_uniform(kbase) + (uint64_t)page * uniform_u64(ksp) + slot * kss_s);
+    pv_b = wave_uniform(wave_uniform(vbase) + (uint64_t)page * uniform_u64(vsp) + slot * vss_s);
+    krs = tile_rsrc(pk_b);
+    vrs = tile_rsrc(pv_b);
     pnvalid = min(kUnitKeys, s.ctx - J0);
     ppage = page;
   }
@@ -1852,7 +1867,8 @@ struct DirectStage {
   // lane-linearly at kbuf + 1 KiB (2 mb + c).  Wave w loads operand mb = w.
   __device__ __forceinline__ void issue_k8(int c, char* kbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gload16_lds(wave_uniform(pk_b + (uint32_t)(16 * wave) * kss + 64u * c), kbuf + 1024 * (2 * wave + c), k8_lane, 0u);
+    const uint32_t kss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)kss);
+    bload16_lds(krs, kbuf + 1024 * (2 * wave + c), k8_lane, (uint32_t)(16 * wave) * kss_s + 64u * c);
   }
   // fp8, d = 128: wave w's V rows 16 w + 8 i + lane / 8 (i = 0, 1), 128 bytes
   // each, lane-linearly into the staging block at v8buf + 1 KiB (2 w + i).
@@ -1860,7 +1876,8 @@ struct DirectStage {
   // them; the block needs no second buffer.
   __device__ __forceinline__ void issue_v8(int i, char* v8buf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gload16_lds(wave_uniform(pv_b + (uint32_t)(16 * wave + 8 * i) * vss), v8buf + 1024 * (2 * wave + i), v8_lane, 0u);
+    const uint32_t vss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)vss);
+    bload16_lds(vrs, v8buf + 1024 * (2 * wave + i), v8_lane, (uint32_t)(16 * wave + 8 * i) * vss_s);
   }
   // After this wave's V DMAs have landed (vmcnt): its 16 rows of fp8 V to
   // bf16 (exact: every E4M3 value is a bf16), written row-major into the V
@@ -1892,8 +1909,10 @@ struct DirectStage {
   }
   __device__ __forceinline__ void issue(int i, char* kbuf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (i < 4) gload16_lds(wave_uniform(pk_b + (uint32_t)(16 * i) * kss), kbuf + 1024 * (4 * i + wave), k_lane, 0u);
-    else gload16_lds(wave_uniform(pv_b + (uint32_t)(16 * (i - 4)) * vss), vbuf + 1024 * (4 * (i - 4) + wave), v_lane, 0u);
+    const uint32_t kss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)kss);
+    const uint32_t vss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)vss);
+    if (i < 4) bload16_lds(krs, kbuf + 1024 * (4 * i + wave), k_lane, (uint32_t)(16 * i) * kss_s);
+    else bload16_lds(vrs, vbuf + 1024 * (4 * (i - 4) + wave), v_lane, (uint32_t)(16 * (i - 4)) * vss_s);
   }
   // after this wave's DMAs into vbuf have landed (vmcnt): zero the V rows it
   // loaded past the sequence end; every lane clears the 16 bytes it wrote
