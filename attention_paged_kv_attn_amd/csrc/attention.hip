@@ -1843,7 +1843,7 @@ struct DirectStage {
   // for i < 4, V rows after).  A DMA holds its wave until the address unit
   // takes it, so the tile loop spreads the eight over its QK MFMAs.
   __device__ __forceinline__ void prep(const KParams& p, const SeqCtx& s, int tile) {
-    const int J0 = tile * kUnitKeys;
+    const int J0 = wave_uniform(tile) * kUnitKeys;     // scalar: the tile may arrive in a VGPR
     const int page = page_of_tile(p, J0);
     const uint32_t slot = (uint32_t)(J0 & page_mask);
     // scalar arithmetic throughout (a stride left in a VGPR would put the
