@@ -201,13 +201,21 @@ __device__ __forceinline__ const KParams& kparams_at(uint64_t v) {
 // Reductions over the four lanes n, n + 16, n + 32, n + 48 that share a query
 // row, with the lane-swap instructions (no LDS round trip): the swap of a
 // register with itself hands each lane both halves of the exchanged pair.
+// max of two scores that are never NaN (masked ones are -inf): a plain
+// v_max_f32, without the quieting copies fmaxf adds for operands the compiler
+// cannot prove canonical (a cross-lane swap's results)
+__device__ __forceinline__ float max_nonan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float row_max4(float x) {
   const unsigned u = __float_as_uint(x);
   auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);      // lanes l & ~16, l | 16
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_nonan(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const unsigned w = __float_as_uint(x);
   auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);      // lanes l & ~32, l | 32
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_nonan(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float row_sum4(float x) {
   const unsigned u = __float_as_uint(x);
@@ -496,13 +504,17 @@ __device__ __forceinline__ void mask_landmarks(f32x4 (&sc)[4], uint64_t lmk, int
 template <int KIND, int D, int NB>
 struct WaveState {
   f32x4 acc[NB][Cfg<KIND, D>::MD];
-  float m2[NB];       // running max of log2-domain scores of this lane's row
+  // reference max m of the log2-domain scores of this lane's row, kept as
+  // nmr = -m (0 while m = -inf) and thr = m + kRescaleSlack (-inf while m = -inf)
+  float nmr[NB], thr[NB];
   float lsum[NB];     // this lane's share of the running sum (reduced at the end)
   f32x4 lacc[NB];     // or: the row's whole running sum, accumulated by MFMA
+  __device__ __forceinline__ float m2(int nb) const { return thr[nb] == kNegInf ? kNegInf : -nmr[nb]; }
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      m2[nb] = kNegInf;
+      nmr[nb] = 0.f;
+      thr[nb] = kNegInf;
       lsum[nb] = 0.f;
       lacc[nb] = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -521,24 +533,32 @@ constexpr float kRescaleSlack = 8.f;
 
 template <int KIND, int D, int NB, bool VSUM = true>
 __device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int nb, f32x4 (&s)[4], float cs) {
-  float mx = kNegInf;
+  float mx = s[0][0];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mb][j]);
+    for (int j = 0; j < 4; ++j)
+      if (mb + j > 0) mx = fmaxf(mx, s[mb][j]);
   mx = row_max4(mx);
-  const float m_cand = mx == kNegInf ? kNegInf : mx * cs;
-  const bool grow = m_cand > st.m2[nb] + kRescaleSlack;
+  // cs > 0, so a row with no visible key keeps m_cand = -inf and never grows
+  const float m_cand = mx * cs;
+  const bool grow = m_cand > st.thr[nb];
   if (__ballot(grow) != 0) {                            // wave-uniform, rare after the first tiles
-    const float m_new = grow ? m_cand : st.m2[nb];
-    const float alpha = st.m2[nb] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st.m2[nb] - m_new);
-    if constexpr (VSUM) st.lsum[nb] *= alpha;
-    else st.lacc[nb] *= alpha;
+    const float m_old = st.m2(nb);
+    const float m_new = grow ? m_cand : m_old;
+    // a row that had no visible key yet holds l = 0 and O = 0: nothing to
+    // rescale (so a segment's first tile skips the multiplies altogether)
+    if (__ballot(grow && m_old != kNegInf) != 0) {
+      const float alpha = m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
+      if constexpr (VSUM) st.lsum[nb] *= alpha;
+      else st.lacc[nb] *= alpha;
 #pragma unroll
-    for (int md = 0; md < Cfg<KIND, D>::MD; ++md) st.acc[nb][md] *= alpha;
-    st.m2[nb] = m_new;
+      for (int md = 0; md < Cfg<KIND, D>::MD; ++md) st.acc[nb][md] *= alpha;
+    }
+    st.nmr[nb] = m_new == kNegInf ? 0.f : -m_new;
+    st.thr[nb] = m_new + kRescaleSlack;
   }
-  const float nmref = st.m2[nb] == kNegInf ? 0.f : -st.m2[nb];
+  const float nmref = st.nmr[nb];
   float sum = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -546,7 +566,7 @@ __device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int n
     for (int j = 0; j < 4; ++j) {
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][j], cs, nmref));
       s[mb][j] = e;
-      if constexpr (VSUM) sum += e;
+      if constexpr (VSUM) sum = mb + j == 0 ? e : sum + e;
     }
   if constexpr (VSUM) st.lsum[nb] += sum;
 }
@@ -1073,7 +1093,7 @@ __device__ PA_SEGMENT_FN void small_segment(uint64_t pk, const QBlock x, int t_l
   float* ls = mrg + kWaves * 16;                       // [wave][16]
   float* os = mrg + 2 * kWaves * 16;                   // [wave][16][D]
   if (h == 0) {
-    ms[wave * 16 + n] = st.m2[0];
+    ms[wave * 16 + n] = st.m2(0);
     ls[wave * 16 + n] = l;
   }
 #pragma unroll
@@ -1325,13 +1345,13 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
         if (n < cx.rows) {
           const bool empty = !(l > 0.f);
           write_row<KIND, D>(p, cx, n, h, st.acc[0], empty ? 0.f : 1.f / l,
-                             empty ? kNegInf : (st.m2[0] + log2f(l)) * kLn2, true, 0);
+                             empty ? kNegInf : (st.m2(0) + log2f(l)) * kLn2, true, 0);
         }
       } else {                                           // cut piece: stash raw state for the merge
         const int k = 2 * wave + (S < wa ? 0 : 1);
         if (lane == 0) tags[k] = cur_q;
         if (h == 0) {
-          stash[SL::M + k * 16 + n] = st.m2[0];
+          stash[SL::M + k * 16 + n] = st.m2(0);
           stash[SL::Lf + k * 16 + n] = l;
         }
 #pragma unroll
@@ -1618,7 +1638,7 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
     if (row_ok) {
       const bool empty = !(l > 0.f);
       write_row<KIND, D>(p, x, ti * p.Hq + head, h, st.acc[0], empty ? 0.f : 1.f / l,
-                         empty ? kNegInf : (st.m2[0] + log2f(l)) * kLn2, final_out, slot);
+                         empty ? kNegInf : (st.m2(0) + log2f(l)) * kLn2, final_out, slot);
     }
     if (!final_out && p.fused) finish_split<KIND, D>(p, q, x, p.n_splits[q], p.slot_base[q]);
   }
@@ -1951,7 +1971,11 @@ __device__ __forceinline__ bf16x8 v_operand_tr(const char* smem, uint32_t trx, u
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
-template <int KIND, int D, bool FAST>
+// LEAN: a build for calls with no block mask and a landmark chunk that is 0 or
+// a multiple of 64, where the only landmark a tile can hold is its last key
+// (offset 63: accumulator slot (3, 3) of lane group 3), so a fully visible
+// tile masks it with one select per row block and the block-mask code is gone.
+template <int KIND, int D, bool FAST, bool LEAN = false>
 __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_lo, int t_hi, int u0,
                                                        int u1, bool final_out, int slot, DirectStage& ds) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -2026,7 +2050,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     left_max = p.window > 0 ? window_left(p, pos_hi_w) : 0;
   }
 
-  const TileParams tp = TileParams::held_of(p);
+  TileParams tp = TileParams::held_of(p);
+  if constexpr (LEAN) tp.has_bm = 0;
   WaveState<KIND, D, NB> st;
   st.init();
   Stage<KIND, D, FAST> stg;
@@ -2120,7 +2145,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           }
         }
         const int nvalid = min(kUnitKeys, x.ctx - J0);
-        const uint64_t lmk = landmark_bits(tp, J0);
+        // LEAN: key J0 + 63 is a landmark when (J0 + 64) is a multiple of the chunk
+        const bool lm63 = LEAN && tp.landmark > 0 &&
+                          (tp.landmark == kUnitKeys || (J0 + kUnitKeys) % tp.landmark == 0);
+        const uint64_t lmk = LEAN ? (lm63 ? uint64_t(1) << (kUnitKeys - 1) : 0) : landmark_bits(tp, J0);
         const bool full = unit_is_full(tp, J0, nvalid, pos_min, left_max);
         // S^T = K Q^T
         f32x4 sc[NB][4];
@@ -2176,15 +2204,18 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
             else
               return *reinterpret_cast<const long*>(kbuf + (i * 64 + lane) * 8);
           };
+          // K-step outermost: the eight accumulators of a step are independent,
+          // so no MFMA waits on the result of the one just issued
+          auto kix = [](int i) { return (i % 4) * C::KSQ + i / 4; };
           KT kr[KDEP];
 #pragma unroll
-          for (int i = 0; i < KDEP; ++i) kr[i] = kread(i);
+          for (int i = 0; i < KDEP; ++i) kr[i] = kread(kix(i));
           __builtin_amdgcn_sched_group_barrier(0x100, KDEP, 0);
 #pragma unroll
           for (int i = 0; i < NK; ++i) {
             const KT ka = kr[i % KDEP];
-            if (i + KDEP < NK) kr[i % KDEP] = kread(i + KDEP);
-            const int mb = i / C::KSQ, ks = i % C::KSQ;
+            if (i + KDEP < NK) kr[i % KDEP] = kread(kix(i + KDEP));
+            const int mb = i % 4, ks = i / 4;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
             if constexpr (DIRECT) { if (i % 2 == 1) ds.issue(i / 2, nkb, nvb); }
@@ -2197,7 +2228,12 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         // shared with the other workgroup's wave it goes ahead of that wave's
         // matrix work instead of queueing behind it (measured faster)
         __builtin_amdgcn_s_setprio(1);
-        if (!full || lmk != 0) {
+        if (LEAN && full) {
+          if (lm63) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sc[nb][3][3] = h == 3 ? kNegInf : sc[nb][3][3];
+          }
+        } else if (!full || lmk != 0) {
           // the lane bitmaps are built from an opaque copy of the landmark
           // bits, so none of that work is hoisted onto the tiles that need
           // no mask at all
@@ -2315,7 +2351,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     if (!rok[nb]) continue;
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : (DKF8 && !v_per_tile ? v_out : 1.f) / l;
-    const float lse = empty ? kNegInf : (st.m2[nb] + log2f(l)) * kLn2;
+    const float lse = empty ? kNegInf : (st.m2(nb) + log2f(l)) * kLn2;
     write_row<KIND, D, TRV>(p, x, rowi[nb], h, st.acc[nb], inv, lse, final_out, slot);
   }
 }
@@ -2369,11 +2405,13 @@ __device__ __forceinline__ void static_items(uint64_t pk) {
 // skips it; the large-only kernel runs the few-row tail Q-blocks of long
 // sequences on the 128-row path (Assign rejects short sequences under it).
 // kPathsHeads is the kernel for sequence Q-blocks (heads_range only).
-constexpr int kPathsAll = 0, kPathsSmall = 1, kPathsLarge = 2, kPathsHeads = 3;
+// kPathsLean is the large-only kernel with large_segment's LEAN build.
+constexpr int kPathsAll = 0, kPathsSmall = 1, kPathsLarge = 2, kPathsHeads = 3, kPathsLean = 4;
 
 template <int KIND, int D, bool FAST, int PATHS>
 __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention_kernel(KParams) {
-  constexpr bool SMALL = PATHS == kPathsSmall, LARGE = PATHS == kPathsLarge, HEADS = PATHS == kPathsHeads;
+  constexpr bool SMALL = PATHS == kPathsSmall, LARGE = PATHS == kPathsLarge || PATHS == kPathsLean,
+                 HEADS = PATHS == kPathsHeads;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint64_t pk = kparams_addr();
   const KParams& p = kparams_at(pk);
@@ -2456,7 +2494,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
         ++q;
         continue;
       } else {
-        large_segment<KIND, D, FAST>(pk, x, t_lo, t_hi, u0, u1, final_out, slot, ds);
+        large_segment<KIND, D, FAST, PATHS == kPathsLean>(pk, x, t_lo, t_hi, u0, u1, final_out, slot, ds);
       }
       if (!final_out && p.fused) finish_split<KIND, D>(p, q, x, p.n_splits[q], p.slot_base[q]);
       a = S + u1;
@@ -2504,6 +2542,13 @@ static hipError_t launch_attention_s(const KParams& p, int kind, int grid, hipSt
 
 hipError_t launch_attention(const KParams& p, int kind, int grid, int paths, hipStream_t stream) {
   if (paths == kPathsHeads) return launch_attention_s<kPathsHeads>(p, kind, grid, stream);
+  // the lean build: bf16 or fp8, d = 128, whole-tile pages, no block mask, a
+  // landmark chunk of 0 or a multiple of 64
+  if (paths == kPathsLarge && kind != KIND_F32 && p.D == 128 && p.page_size >= kUnitKeys && p.bm == nullptr &&
+      p.landmark % kUnitKeys == 0) {
+    return kind == KIND_BF16 ? launch_attention_t<KIND_BF16, 128, true, kPathsLean>(p, grid, stream)
+                             : launch_attention_t<KIND_F8, 128, true, kPathsLean>(p, grid, stream);
+  }
   if (paths == kPathsSmall) return launch_attention_s<kPathsSmall>(p, kind, grid, stream);
   if (paths == kPathsLarge) return launch_attention_s<kPathsLarge>(p, kind, grid, stream);
   return launch_attention_s<kPathsAll>(p, kind, grid, stream);

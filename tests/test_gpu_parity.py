@@ -357,6 +357,21 @@ def test_sliding_window_reduced():
     compare(b, out, lse)
 
 
+@pytest.mark.parametrize("chunk", [32, 64, 128, 192])
+def test_sliding_window_landmark_chunks(chunk):
+    """Landmark chunks that are multiples of 64 (one landmark at most per
+    64-key tile, on its last key: the lean kernel build) and one that is not
+    (several per tile: the general build), each against the oracle, with Q = 0
+    as well (LSE = ln of the visible-key count)."""
+    b = W.sliding_window(seq_len=1600, window=600, landmark_chunk=chunk)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+    b.q = torch.zeros_like(b.q)
+    g, out, lse, ws = gpu_run(b)
+    compare(b, out, lse)
+
+
 def test_sliding_window_full_size_sampled(golden):
     b = W.sliding_window()
     g, out, lse, ws = gpu_run(b)
