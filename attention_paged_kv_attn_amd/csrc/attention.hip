@@ -1795,12 +1795,21 @@ struct DirectStage {
   uint32_t k_lane, v_lane;    // byte offsets of the lane's rows for load i = 0
   uint32_t k8_lane;           // fp8 K (see issue_k8): row m, byte 16 hh of a 64-byte chunk
   uint32_t v8_lane;           // fp8 V (see issue_v8): row lane / 8, bytes 16 (lane % 8) ..
+  // Segment-constant addressing (SEG; the host selects it only where every
+  // byte of the K and of the V cache lies within 2^31 of its head's base):
+  // one buffer resource per sequence and kv head, a tile's page and slot as
+  // one 32-bit scalar offset, and every DMA's row offset held per lane, so a
+  // tile costs a page lookup and two scalar multiplies.
+  __amdgpu_buffer_rsrc_t krs_seg, vrs_seg;
+  uint32_t ktoff, vtoff;      // the prepared tile's byte offsets from kbase / vbase
+  uint32_t ko[4], vo[4];      // per lane: offsets of DMA i (K) and 4 + i (V) within a tile
+  uint32_t k8o[2], v8o[2];    // per lane: offsets of the fp8 DMAs (issue_k8, issue_v8)
 
   // (re)point at sequence s.b, kv head s.g; the page window survives while the
   // sequence stays the same
   // ELT: bytes per K/V element (the direct loads are bf16; other kinds use
   // only the page window)
-  template <int ELT = 2>
+  template <int ELT = 2, bool SEG = false>
   __device__ __forceinline__ void init(const KParams& p, const SeqCtx& s) {
     if (s.b == cur_b && s.g == cur_g) return;
     if (s.b != cur_b) pbase = -(1 << 30);
@@ -1828,6 +1837,20 @@ struct DirectStage {
     v_lane = (uint32_t)v_row0 * vss + v_col;
     k8_lane = (uint32_t)m * kss + 16u * hh;
     v8_lane = (uint32_t)(lane >> 3) * vss + 16u * (lane & 7);
+    if constexpr (SEG) {
+      krs_seg = tile_rsrc(kbase);
+      vrs_seg = tile_rsrc(vbase);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ko[i] = k_lane + (uint32_t)(16 * i) * kss;
+        vo[i] = v_lane + (uint32_t)(16 * i) * vss;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        k8o[i] = k8_lane + (uint32_t)(16 * wave) * kss + 64u * i;
+        v8o[i] = v8_lane + (uint32_t)(16 * wave + 8 * i) * vss;
+      }
+    }
   }
 
   __device__ __forceinline__ int page_of_tile(const KParams& p, int J0) {
@@ -1862,6 +1885,7 @@ struct DirectStage {
   // The addresses of one tile's DMAs; issue(i) then starts DMA i of 8 (K rows
   // for i < 4, V rows after).  A DMA holds its wave until the address unit
   // takes it, so the tile loop spreads the eight over its QK MFMAs.
+  template <bool SEG = false>
   __device__ __forceinline__ void prep(const KParams& p, const SeqCtx& s, int tile) {
     const int J0 = wave_uniform(tile) * kUnitKeys;     // scalar: the tile may arrive in a VGPR
     const int page = page_of_tile(p, J0);
@@ -1870,6 +1894,13 @@ struct DirectStage {
     // products on the VALU and read them back)
     const uint32_t kss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)kss);
     const uint32_t vss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)vss);
+    if constexpr (SEG) {
+      ktoff = (uint32_t)wave_uniform((int)((uint32_t)page * (uint32_t)uniform_u64(ksp) + slot * kss_s));
+      vtoff = (uint32_t)wave_uniform((int)((uint32_t)page * (uint32_t)uniform_u64(vsp) + slot * vss_s));
+      pnvalid = min(kUnitKeys, s.ctx - J0);
+      ppage = page;
+      return;
+    }
     pk_b = wave_uniform(wave_uniform(kbase) + (uint64_t)page * uniform_u64(ksp) + slot * kss_s);
     pv_b = wave_uniform(wave_uniform(vbase) + (uint64_t)page * uniform_u64(vsp) + slot * vss_s);
     krs = tile_rsrc(pk_b);
@@ -1885,8 +1916,13 @@ struct DirectStage {
   // 16x16x128 MFMA with each lane's 32 bytes taken as two 16-byte chunks:
   // chunk c of operand mb (rows 16 mb + m, bytes 64 c + 16 hh) lands
   // lane-linearly at kbuf + 1 KiB (2 mb + c).  Wave w loads operand mb = w.
+  template <bool SEG = false>
   __device__ __forceinline__ void issue_k8(int c, char* kbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (SEG) {
+      bload16_lds(krs_seg, kbuf + 1024 * (2 * wave + c), k8o[c], ktoff);
+      return;
+    }
     const uint32_t kss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)kss);
     bload16_lds(krs, kbuf + 1024 * (2 * wave + c), k8_lane, (uint32_t)(16 * wave) * kss_s + 64u * c);
   }
@@ -1894,8 +1930,13 @@ struct DirectStage {
   // each, lane-linearly into the staging block at v8buf + 1 KiB (2 w + i).
   // Only wave w reads them back (widen_v8), so the wave's own wait orders
   // them; the block needs no second buffer.
+  template <bool SEG = false>
   __device__ __forceinline__ void issue_v8(int i, char* v8buf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (SEG) {
+      bload16_lds(vrs_seg, v8buf + 1024 * (2 * wave + i), v8o[i], vtoff);
+      return;
+    }
     const uint32_t vss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)vss);
     bload16_lds(vrs, v8buf + 1024 * (2 * wave + i), v8_lane, (uint32_t)(16 * wave + 8 * i) * vss_s);
   }
@@ -1927,8 +1968,14 @@ struct DirectStage {
       *reinterpret_cast<u32x4*>(row + 16 * ((2 * q + 1) ^ sw)) = hi;
     }
   }
+  template <bool SEG = false>
   __device__ __forceinline__ void issue(int i, char* kbuf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (SEG) {
+      if (i < 4) bload16_lds(krs_seg, kbuf + 1024 * (4 * i + wave), ko[i], ktoff);
+      else bload16_lds(vrs_seg, vbuf + 1024 * (4 * (i - 4) + wave), vo[i - 4], vtoff);
+      return;
+    }
     const uint32_t kss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)kss);
     const uint32_t vss_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)vss);
     if (i < 4) bload16_lds(krs, kbuf + 1024 * (4 * i + wave), k_lane, (uint32_t)(16 * i) * kss_s);
@@ -1945,10 +1992,11 @@ struct DirectStage {
       if (v_row0 + 16 * i >= pnvalid)
         *reinterpret_cast<u32x4*>(vbuf + 1024 * (4 * i + wave) + 16 * lane) = u32x4{0, 0, 0, 0};
   }
+  template <bool SEG = false>
   __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
-    prep(p, s, tile);
+    prep<SEG>(p, s, tile);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) issue(i, kbuf, vbuf);
+    for (int i = 0; i < 8; ++i) issue<SEG>(i, kbuf, vbuf);
   }
 };
 
@@ -1974,7 +2022,8 @@ __device__ __forceinline__ bf16x8 v_operand_tr(const char* smem, uint32_t trx, u
 // LEAN: a build for calls with no block mask and a landmark chunk that is 0 or
 // a multiple of 64, where the only landmark a tile can hold is its last key
 // (offset 63: accumulator slot (3, 3) of lane group 3), so a fully visible
-// tile masks it with one select per row block and the block-mask code is gone.
+// tile masks it with one select per row block and the block-mask code is gone;
+// its DMAs use the segment-constant addressing of DirectStage (SEG).
 template <int KIND, int D, bool FAST, bool LEAN = false>
 __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_lo, int t_hi, int u0,
                                                        int u1, bool final_out, int slot, DirectStage& ds) {
@@ -2065,7 +2114,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     v_per_tile = held((p.scale_mode & 3) == 2 ? 1 : 0) != 0;
     v_out = v_per_tile ? 1.f : p.v_scale[0];
   }
-  if constexpr (FAST) ds.init<C::ELT>(p, s);       // keeps its page window while the sequence stays
+  if constexpr (FAST) ds.init<C::ELT, LEAN>(p, s);       // keeps its page window while the sequence stays
 
   for (int c0 = u0; c0 < u1; c0 += kMaskListCap) {
     const int cn = min(kMaskListCap, u1 - c0);
@@ -2074,15 +2123,15 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       return __builtin_amdgcn_readfirstlane(tp.has_bm ? (int)list[u - c0] : t_lo + u);
     };
     if constexpr (DIRECT) {
-      ds.load(p, s, tile_of(c0), smem, vstage<true>(0));
+      ds.load<LEAN>(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
       ds.zero_tail(vstage<true>(0));
     } else if constexpr (DKF8) {
-      ds.prep(p, s, tile_of(c0));
-      ds.issue_k8(0, smem);
-      ds.issue_k8(1, smem);
-      ds.issue_v8(0, v8buf);
-      ds.issue_v8(1, v8buf);
+      ds.prep<LEAN>(p, s, tile_of(c0));
+      ds.issue_k8<LEAN>(0, smem);
+      ds.issue_k8<LEAN>(1, smem);
+      ds.issue_v8<LEAN>(0, v8buf);
+      ds.issue_v8<LEAN>(1, v8buf);
       cur_ksc = kscale_at_page<KIND>(p, s, ds.ppage, &cur_vsc);
       wait_vmem();
       ds.widen_v8(v8buf, vstage<true>(0));
@@ -2107,20 +2156,20 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         // the next tile's K and V go out before the QK MFMAs (a chunk's last
         // step re-loads its own tile into the idle stage, as the bf16 path)
         nvb = vstage<true>(buf ^ 1);
-        ds.prep(p, s, tile_of(more ? u + 1 : u));
-        ds.issue_k8(0, nkb);
-        ds.issue_k8(1, nkb);
-        ds.issue_v8(0, v8buf);
-        ds.issue_v8(1, v8buf);
+        ds.prep<LEAN>(p, s, tile_of(more ? u + 1 : u));
+        ds.issue_k8<LEAN>(0, nkb);
+        ds.issue_k8<LEAN>(1, nkb);
+        ds.issue_v8<LEAN>(0, v8buf);
+        ds.issue_v8<LEAN>(1, v8buf);
         nksc = kscale_at_page<KIND>(p, s, ds.ppage, &nvsc);
       } else if constexpr (DIRECT) {
         // the next tile's DMAs go out between the QK MFMAs below (the last
         // step of a chunk re-loads its own tile into the idle stage)
         nvb = vstage<true>(buf ^ 1);
-        ds.prep(p, s, tile_of(more ? u + 1 : u));
+        ds.prep<LEAN>(p, s, tile_of(more ? u + 1 : u));
         if (!wave_live) {                               // a wave with no rows still loads its share
 #pragma unroll
-          for (int i = 0; i < 8; ++i) ds.issue(i, nkb, nvb);
+          for (int i = 0; i < 8; ++i) ds.issue<LEAN>(i, nkb, nvb);
         }
       } else if (more) {
         stg.load(p, s, tile_of(u + 1), FAST ? ds.page_of_tile(p, tile_of(u + 1) * kUnitKeys) : -1);
@@ -2218,7 +2267,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
             const int mb = i % 4, ks = i / 4;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
-            if constexpr (DIRECT) { if (i % 2 == 1) ds.issue(i / 2, nkb, nvb); }
+            if constexpr (DIRECT) { if (i % 2 == 1) ds.issue<LEAN>(i / 2, nkb, nvb); }
             __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
             if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             if constexpr (DIRECT) { if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); }
@@ -2543,9 +2592,15 @@ static hipError_t launch_attention_s(const KParams& p, int kind, int grid, hipSt
 hipError_t launch_attention(const KParams& p, int kind, int grid, int paths, hipStream_t stream) {
   if (paths == kPathsHeads) return launch_attention_s<kPathsHeads>(p, kind, grid, stream);
   // the lean build: bf16 or fp8, d = 128, whole-tile pages, no block mask, a
-  // landmark chunk of 0 or a multiple of 64
+  // landmark chunk of 0 or a multiple of 64, and K and V caches whose bytes
+  // (any page, slot and dim of a head) lie within 2^31 of the head's base, so
+  // that its DMAs address them with 32-bit offsets from one buffer resource
+  const int64_t elt = kind == KIND_BF16 ? 2 : 1;
+  auto span_ok = [&](int64_t sp, int64_t ss) {
+    return sp > 0 && ss > 0 && (int64_t(p.num_pages) * sp + int64_t(kUnitKeys) * ss + p.D) * elt < (int64_t(1) << 31);
+  };
   if (paths == kPathsLarge && kind != KIND_F32 && p.D == 128 && p.page_size >= kUnitKeys && p.bm == nullptr &&
-      p.landmark % kUnitKeys == 0) {
+      p.landmark % kUnitKeys == 0 && span_ok(p.k_sp, p.k_ss) && span_ok(p.v_sp, p.v_ss)) {
     return kind == KIND_BF16 ? launch_attention_t<KIND_BF16, 128, true, kPathsLean>(p, grid, stream)
                              : launch_attention_t<KIND_F8, 128, true, kPathsLean>(p, grid, stream);
   }
