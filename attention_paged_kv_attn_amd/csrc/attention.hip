@@ -1944,16 +1944,23 @@ struct DirectStage {
   // bf16 (exact: every E4M3 value is a bf16), written row-major into the V
   // stage with the bf16 direct path's swizzle (16-byte chunk q of row r in
   // slot q ^ 2 (r % 8)).  Rows past the sequence end (the last tile only) are
-  // written as zeros, so no garbage (NaN included) reaches P V.
+  // written as zeros, so no garbage (NaN included) reaches P V.  A lane of an
+  // odd row takes its two 8-byte halves in the other order, so the 16 lanes of
+  // one LDS write (two rows) fill both the even and the odd chunk slots: no
+  // bank conflicts (measured 2% faster dense fp8 prefill).
   __device__ __forceinline__ void widen_v8(const char* v8buf, char* vbuf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 16 * wave + 8 * i + (lane >> 3), q = lane & 7;    // fp8 bytes 16 q .. 16 q + 15 of row r
-      u32x4 raw = *reinterpret_cast<const u32x4*>(v8buf + 1024 * (2 * wave + i) + 16 * lane);
+      const int odd = (lane >> 3) & 1;                              // r & 1
+      const char* src = v8buf + 1024 * (2 * wave + i) + 16 * lane;
+      const u32x2 f0 = *reinterpret_cast<const u32x2*>(src + 8 * odd);
+      const u32x2 f1 = *reinterpret_cast<const u32x2*>(src + 8 * (1 - odd));
+      u32x4 raw = u32x4{f0[0], f0[1], f1[0], f1[1]};
       if (pnvalid < kUnitKeys && r >= pnvalid) raw = u32x4{0, 0, 0, 0};
-      u32x4 lo, hi;                                                  // bf16 dims 16 q .. + 7, 16 q + 8 .. + 15
+      u32x4 lo, hi;          // bf16 of fp8 bytes 16 q + 8 odd .. + 7 and 16 q + 8 (1 - odd) .. + 7
       lo[0] = f8x2_to_bf16x2(raw[0]);
       lo[1] = f8x2_to_bf16x2<true>(raw[0]);
       lo[2] = f8x2_to_bf16x2(raw[1]);
@@ -1964,8 +1971,8 @@ struct DirectStage {
       hi[3] = f8x2_to_bf16x2<true>(raw[3]);
       char* row = vbuf + 256 * r;
       const int sw = 2 * (r & 7);
-      *reinterpret_cast<u32x4*>(row + 16 * ((2 * q) ^ sw)) = lo;
-      *reinterpret_cast<u32x4*>(row + 16 * ((2 * q + 1) ^ sw)) = hi;
+      *reinterpret_cast<u32x4*>(row + 16 * ((2 * q + odd) ^ sw)) = lo;
+      *reinterpret_cast<u32x4*>(row + 16 * ((2 * q + 1 - odd) ^ sw)) = hi;
     }
   }
   template <bool SEG = false>
