@@ -879,6 +879,17 @@ __device__ __forceinline__ void mask_scores(f32x4 (&sc)[4], const ElemMask& em, 
       sc[mb][j] = ok ? sc[mb][j] : kNegInf;
     }
 }
+// The same mask as an additive bias (0 where visible, -inf where masked).
+__device__ __forceinline__ void mask_bias(f32x4 (&bias)[4], const ElemMask& em, int h) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = 16 * mb + 4 * h + j;
+      const bool ok = ((unsigned)(o - em.lo) < em.span) && !((em.l16 >> (4 * mb + j)) & 1u);
+      bias[mb][j] = ok ? 0.f : kNegInf;
+    }
+}
 
 // Q operands of a small Q-block, staged in LDS (element ks * 64 + lane holds
 // lane's operand of K-step ks) or held in the lane's registers.
@@ -1909,9 +1920,10 @@ struct DirectStage {
     ppage = page;
   }
   // The tile lies in one page, so rows past the sequence end are still cache
-  // memory: they are read as they are (their scores are masked by select)
-  // and their V rows are zeroed once landed (zero_tail), so no garbage reaches
-  // P V.  Row 16 i of a load moves the scalar base only.
+  // memory: they are read as they are, their V rows (and in the lean build,
+  // which masks by an additive bias, their K rows) are zeroed once landed
+  // (zero_tail), and their scores are masked, so no garbage (NaN included)
+  // reaches a score or P V.  Row 16 i of a load moves the scalar base only.
   // fp8, d = 128: the K tile straight to LDS in the operand order of the
   // 16x16x128 MFMA with each lane's 32 bytes taken as two 16-byte chunks:
   // chunk c of operand mb (rows 16 mb + m, bytes 64 c + 16 hh) lands
@@ -1988,16 +2000,33 @@ struct DirectStage {
     if (i < 4) bload16_lds(krs, kbuf + 1024 * (4 * i + wave), k_lane, (uint32_t)(16 * i) * kss_s);
     else bload16_lds(vrs, vbuf + 1024 * (4 * (i - 4) + wave), v_lane, (uint32_t)(16 * (i - 4)) * vss_s);
   }
-  // after this wave's DMAs into vbuf have landed (vmcnt): zero the V rows it
-  // loaded past the sequence end; every lane clears the 16 bytes it wrote
-  __device__ __forceinline__ void zero_tail(char* vbuf) {
+  // after this wave's DMAs into kbuf and vbuf have landed (vmcnt): zero the
+  // V rows (and with K, the K rows) it loaded past the sequence end; every
+  // lane clears the 16 bytes it wrote (K load i holds rows 16 i + lane % 16,
+  // see issue)
+  template <bool K>
+  __device__ __forceinline__ void zero_tail(char* kbuf, char* vbuf) {
     if (pnvalid >= kUnitKeys) return;                     // uniform: only a sequence's last tile
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if (K && k_row0 + 16 * i >= pnvalid)
+        *reinterpret_cast<u32x4*>(kbuf + 1024 * (4 * i + wave) + 16 * lane) = u32x4{0, 0, 0, 0};
       if (v_row0 + 16 * i >= pnvalid)
         *reinterpret_cast<u32x4*>(vbuf + 1024 * (4 * i + wave) + 16 * lane) = u32x4{0, 0, 0, 0};
+    }
+  }
+  // fp8: the same for the K rows of issue_k8 (wave w: rows 16 w + lane % 16)
+  __device__ __forceinline__ void zero_tail_k8(char* kbuf) {
+    if (pnvalid >= kUnitKeys) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (16 * wave + (lane & 15) >= pnvalid) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        *reinterpret_cast<u32x4*>(kbuf + 1024 * (2 * wave + c) + 16 * lane) = u32x4{0, 0, 0, 0};
+    }
   }
   template <bool SEG = false>
   __device__ __forceinline__ void load(const KParams& p, const SeqCtx& s, int tile, char* kbuf, char* vbuf) {
@@ -2132,7 +2161,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     if constexpr (DIRECT) {
       ds.load<LEAN>(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
-      ds.zero_tail(vstage<true>(0));
+      ds.zero_tail<LEAN>(smem, vstage<true>(0));
     } else if constexpr (DKF8) {
       ds.prep<LEAN>(p, s, tile_of(c0));
       ds.issue_k8<LEAN>(0, smem);
@@ -2141,6 +2170,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       ds.issue_v8<LEAN>(1, v8buf);
       cur_ksc = kscale_at_page<KIND>(p, s, ds.ppage, &cur_vsc);
       wait_vmem();
+      if constexpr (LEAN) ds.zero_tail_k8(smem);
       ds.widen_v8(v8buf, vstage<true>(0));
     } else {
       stg.load(p, s, tile_of(c0), FAST ? ds.page_of_tile(p, tile_of(c0) * kUnitKeys) : -1);
@@ -2206,12 +2236,21 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
                           (tp.landmark == kUnitKeys || (J0 + kUnitKeys) % tp.landmark == 0);
         const uint64_t lmk = LEAN ? (lm63 ? uint64_t(1) << (kUnitKeys - 1) : 0) : landmark_bits(tp, J0);
         const bool full = unit_is_full(tp, J0, nvalid, pos_min, left_max);
-        // S^T = K Q^T
+        // S^T = K Q^T.  The lean build takes a tile's mask as the initial
+        // accumulator of its QK MFMAs (0 where a score is visible, -inf where
+        // masked), so masked and unmasked tiles leave their scores in the same
+        // registers with no select after the products (a select there makes
+        // the compiler copy all 32 scores on every unmasked tile).  Keys past
+        // the sequence end are zeros in LDS (zero_tail), so a masked score is
+        // -inf, never NaN.  The other builds select after the products: the
+        // 32 bias registers would push them into spills.
         f32x4 sc[NB][4];
+        if constexpr (!LEAN) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) sc[nb][mb] = f32x4{0, 0, 0, 0};
+            for (int mb = 0; mb < 4; ++mb) sc[nb][mb] = f32x4{0, 0, 0, 0};
+        }
         if constexpr (KIND == KIND_F32) {
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
@@ -2223,13 +2262,12 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka[i], qB[nb][4 * cc + i], sc[nb][mb]);
             }
-        } else if constexpr (KIND == KIND_F8 && D == 128) {
-          // one 16x16x128 MFMA per (mb, nb); the next mb's four K operands are
-          // read while this mb's MFMAs run
-          i32x8 qc[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) qc[nb] = cat4(qB[nb][0], qB[nb][1], qB[nb][2], qB[nb][3]);
-          auto kread4 = [&](int mb) -> i32x8 {
+        } else {
+          // K operand reads.  fp8: the first operand goes out ahead of the
+          // branch on the tile's mask below, so its latency does not wait on
+          // it (bf16 keeps its first reads in the branches: eight operands
+          // held across the mask's bias would spill)
+          auto kread4 = [&](int mb) -> i32x8 {            // fp8, d = 128: operand mb
             if constexpr (DKF8) {
               const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + 1024 * (2 * mb) + 16 * lane);
               const u32x4 b = *reinterpret_cast<const u32x4*>(kbuf + 1024 * (2 * mb + 1) + 16 * lane);
@@ -2240,21 +2278,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
                           *reinterpret_cast<const long*>(at + 1024), *reinterpret_cast<const long*>(at + 1536));
             }
           };
-          i32x8 kc = kread4(0);
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            const i32x8 ka = kc;
-            if (mb + 1 < 4) kc = kread4(mb + 1);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk128(ka, qc[nb], sc[nb][mb]);
-          }
-        } else {
-          // K operands stream from LDS KDEP reads ahead of the MFMAs that use
-          // them (the schedule groups below keep that order), so the reads'
-          // latency hides behind the matrix work instead of stalling each MFMA
-          constexpr int NK = 4 * C::KSQ, KDEP = 8;
           using KT = typename QKOpT<KIND>::T;
-          auto kread = [&](int i) -> KT {
+          auto kread = [&](int i) -> KT {                 // other kinds: operand i
             if constexpr (KIND == KIND_BF16)
               return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + (i * 64 + lane) * 16));
             else
@@ -2262,47 +2287,92 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
           };
           // K-step outermost: the eight accumulators of a step are independent,
           // so no MFMA waits on the result of the one just issued
+          constexpr int NK = 4 * C::KSQ, KDEP = 8;
           auto kix = [](int i) { return (i % 4) * C::KSQ + i / 4; };
-          KT kr[KDEP];
+          constexpr bool QK128 = KIND == KIND_F8 && D == 128;
+          i32x8 kc0;
+          if constexpr (QK128) kc0 = kread4(0);
+          // init(nb, mb): the lean build's initial accumulator of row-block nb,
+          // key block mb (the other builds start from the zeros above)
+          auto qk = [&](auto init) {
+            if constexpr (QK128) {
+              // one 16x16x128 MFMA per (mb, nb); the next mb's four K operands
+              // are read while this mb's MFMAs run
+              i32x8 qc[NB];
 #pragma unroll
-          for (int i = 0; i < KDEP; ++i) kr[i] = kread(kix(i));
-          __builtin_amdgcn_sched_group_barrier(0x100, KDEP, 0);
+              for (int nb = 0; nb < NB; ++nb) qc[nb] = cat4(qB[nb][0], qB[nb][1], qB[nb][2], qB[nb][3]);
+              i32x8 kc = kc0;
 #pragma unroll
-          for (int i = 0; i < NK; ++i) {
-            const KT ka = kr[i % KDEP];
-            if (i + KDEP < NK) kr[i % KDEP] = kread(kix(i + KDEP));
-            const int mb = i % 4, ks = i / 4;
+              for (int mb = 0; mb < 4; ++mb) {
+                const i32x8 ka = kc;
+                if (mb + 1 < 4) kc = kread4(mb + 1);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], sc[nb][mb]);
-            if constexpr (DIRECT) { if (i % 2 == 1) ds.issue<LEAN>(i / 2, nkb, nvb); }
-            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
-            if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if constexpr (DIRECT) { if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); }
+                for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk128(ka, qc[nb], LEAN ? init(nb, mb) : sc[nb][mb]);
+              }
+            } else {
+              // K operands stream from LDS KDEP reads ahead of the MFMAs that
+              // use them (the schedule groups below keep that order), so the
+              // reads' latency hides behind the matrix work instead of
+              // stalling each MFMA
+              KT kr[KDEP];
+#pragma unroll
+              for (int i = 0; i < KDEP; ++i) kr[i] = kread(kix(i));
+              __builtin_amdgcn_sched_group_barrier(0x100, KDEP, 0);
+#pragma unroll
+              for (int i = 0; i < NK; ++i) {
+                const KT ka = kr[i % KDEP];
+                if (i + KDEP < NK) kr[i % KDEP] = kread(kix(i + KDEP));
+                const int mb = i % 4, ks = i / 4;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], LEAN && ks == 0 ? init(nb, mb) : sc[nb][mb]);
+                if constexpr (DIRECT) { if (i % 2 == 1) ds.issue<LEAN>(i / 2, nkb, nvb); }
+                __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+                if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if constexpr (DIRECT) { if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); }
+              }
+            }
+          };
+          const auto zero_init = [](int, int) { return f32x4{0, 0, 0, 0}; };
+          if (!LEAN || (full && lmk == 0)) {
+            qk(zero_init);
+          } else if (full) {
+            // LEAN: the only landmark of a full tile is key 63, slot (3, 3) of
+            // lane group 3
+            const f32x4 lmb = f32x4{0, 0, 0, h == 3 ? kNegInf : 0.f};
+            qk([&](int, int mb) { return mb == 3 ? lmb : f32x4{0, 0, 0, 0}; });
+          } else {
+            // a tile that is not full; the lane bitmaps are built from an
+            // opaque copy of the landmark bits, so none of that work is
+            // hoisted onto the tiles that need no mask at all
+            uint64_t lm = lmk;
+            asm volatile("" : "+s"(lm));
+            f32x4 bias[NB][4];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              ElemMask em;
+              em.init(tp, rm[nb], J0, nvalid, lm, h);
+              mask_bias(bias[nb], em, h);
+            }
+            qk([&](int nb, int mb) { return bias[nb][mb]; });
           }
         }
         // the softmax (VALU work) runs at raised wave priority, so on a SIMD
         // shared with the other workgroup's wave it goes ahead of that wave's
         // matrix work instead of queueing behind it (measured faster)
         __builtin_amdgcn_s_setprio(1);
-        if (LEAN && full) {
-          if (lm63) {
+        if constexpr (!LEAN) {
+          if (!full || lmk != 0) {
+            uint64_t lm = lmk;
+            asm volatile("" : "+s"(lm));
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) sc[nb][3][3] = h == 3 ? kNegInf : sc[nb][3][3];
-          }
-        } else if (!full || lmk != 0) {
-          // the lane bitmaps are built from an opaque copy of the landmark
-          // bits, so none of that work is hoisted onto the tiles that need
-          // no mask at all
-          uint64_t lm = lmk;
-          asm volatile("" : "+s"(lm));
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            if (!full) {
-              ElemMask em;
-              em.init(tp, rm[nb], J0, nvalid, lm, h);
-              mask_scores(sc[nb], em, h);
-            } else {
-              mask_landmarks(sc[nb], lm, h);
+            for (int nb = 0; nb < NB; ++nb) {
+              if (!full) {
+                ElemMask em;
+                em.init(tp, rm[nb], J0, nvalid, lm, h);
+                mask_scores(sc[nb], em, h);
+              } else {
+                mask_landmarks(sc[nb], lm, h);
+              }
             }
           }
         }
@@ -2382,9 +2452,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (DIRECT) {
         wait_vmem();
-        ds.zero_tail(nvb);
+        ds.zero_tail<LEAN>(nkb, nvb);
       } else if constexpr (DKF8) {
         wait_vmem();                                     // this wave's K and V DMAs have landed
+        if constexpr (LEAN) ds.zero_tail_k8(nkb);
         ds.widen_v8(v8buf, nvb);
         cur_ksc = nksc;
         cur_vsc = nvsc;

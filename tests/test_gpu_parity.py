@@ -524,6 +524,31 @@ def test_prefill_kernel_choice_by_q_len_bound(kind):
     compare(b, out2, lse2)
 
 
+@pytest.mark.parametrize("kind,mode", [("bf16", None), ("e4m3", "tensor"), ("e4m3", "page_head")])
+def test_large_qblocks_ragged_tails_poisoned(kind, mode):
+    """Large-Q-block runs (the lean build: d 128, 64-token pages, no block
+    mask) whose sequences end inside a 64-key tile, with every cache slot past
+    the ends poisoned (NaN in bf16, 0x7F in FP8), whole and chunked prefill
+    mixed: the keys past an end are zeroed in LDS and masked, so no poison
+    reaches O or the LSE."""
+    rng = np.random.default_rng(21)
+    b = W.build_batch(rng, name=f"ragged_large_{kind}_{mode}", kind=kind, Hq=32, Hkv=8, d=128, page_size=64,
+                      ctx=[1000, 1537, 130, 777], q_len=[1000, 600, 130, 777], quant_mode=mode, poison=True)
+    assert b.min_q_len == 130
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
+def test_sliding_window_ragged_tail_poisoned():
+    """The sliding-window forward (landmarks every 64 keys: the lean build)
+    over a sequence that ends inside a tile, its pages' free slots poisoned."""
+    b = W.sliding_window(seq_len=1000, window=300)
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
 @pytest.mark.parametrize("make,kw", [
     (lambda: W.splitk_decode(q_len=1, batch=16, ctx_lo=64, ctx_hi=6000), {}),
     (lambda: W.splitk_decode(q_len=[1, 2, 4, 3] * 4, batch=16, ctx_lo=64, ctx_hi=6000), {"max_q_len": 0}),
