@@ -209,6 +209,11 @@ __device__ __forceinline__ float max_nonan(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+__device__ __forceinline__ float max3_nonan(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float row_max4(float x) {
   const unsigned u = __float_as_uint(x);
   auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);      // lanes l & ~16, l | 16
@@ -533,17 +538,18 @@ constexpr float kRescaleSlack = 8.f;
 
 template <int KIND, int D, int NB, bool VSUM = true>
 __device__ __forceinline__ void softmax_update(WaveState<KIND, D, NB>& st, int nb, f32x4 (&s)[4], float cs) {
-  float mx = s[0][0];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (mb + j > 0) mx = fmaxf(mx, s[mb][j]);
-  mx = row_max4(mx);
-  // cs > 0, so a row with no visible key keeps m_cand = -inf and never grows
-  const float m_cand = mx * cs;
-  const bool grow = m_cand > st.thr[nb];
-  if (__ballot(grow) != 0) {                            // wave-uniform, rare after the first tiles
+  // this lane's 16 scores (the row's other 48 sit in lanes n + 16, 32, 48)
+  const float m0 = max3_nonan(s[0][0], s[0][1], s[0][2]), m1 = max3_nonan(s[0][3], s[1][0], s[1][1]);
+  const float m2 = max3_nonan(s[1][2], s[1][3], s[2][0]), m3 = max3_nonan(s[2][1], s[2][2], s[2][3]);
+  const float m4 = max3_nonan(s[3][0], s[3][1], s[3][2]);
+  const float mx = max_nonan(max3_nonan(m0, m1, m2), max3_nonan(m3, m4, s[3][3]));
+  // The threshold is the same in the four lanes of a row, so some lane's max
+  // exceeds it exactly when the row's max does: the cross-lane reduction is
+  // needed only on that (rare) path.  cs > 0, so a row with no visible key
+  // keeps its max at -inf and never grows.
+  if (__ballot(mx * cs > st.thr[nb]) != 0) {            // wave-uniform, rare after the first tiles
+    const float m_cand = row_max4(mx) * cs;
+    const bool grow = m_cand > st.thr[nb];
     const float m_old = st.m2(nb);
     const float m_new = grow ? m_cand : m_old;
     // a row that had no visible key yet holds l = 0 and O = 0: nothing to
