@@ -93,6 +93,11 @@ struct Lds {
   static constexpr int TOTAL = DYN + (SPLIT_V ? 2 * kVStageBytes : 0);
   static constexpr int OCC = TOTAL <= 80 * 1024 ? 2 : 1;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  // the lean bf16 build: three K stages and nothing else in the dynamic block
+  // (with the two V stages exactly 80 KiB, so two workgroups share a CU)
+  static constexpr int DYN_LEAN = KIND == KIND_BF16 ? 3 * C::K_TILE : DYN;
+  static_assert(KIND != KIND_BF16 || !SPLIT_V || DYN_LEAN + 2 * kVStageBytes <= 80 * 1024, "lean LDS budget");
+  static_assert(DYN_LEAN >= 256 * 40 + 4, "fused merge slots");
   static_assert(!SPLIT_V || 2 * 16 * D * 4 <= kVStageBytes, "two stash pieces per V stage");
 };
 
@@ -1013,7 +1018,9 @@ __device__ __forceinline__ void small_compute(const KParams& p, const SeqCtx& s,
 template <int KIND, int D>
 __device__ void finish_split(const KParams& p, int q, const QBlock& x, int ns, int sb) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int last;
+  // the flag sits in the dynamic block past the merge's 256 reduction slots
+  // (a static variable would take LDS that the lean build's stages fill)
+  int& last = *reinterpret_cast<int*>(smem + 256 * sizeof(MergeState));
   // Publication: every thread's partial stores (device-coherent) are complete
   // before the barrier, and after it one thread counts the piece with an
   // agent-scope release; the workgroup that brings the count to ns acquires
@@ -2006,20 +2013,30 @@ struct DirectStage {
     if (i < 4) bload16_lds(krs, kbuf + 1024 * (4 * i + wave), k_lane, (uint32_t)(16 * i) * kss_s);
     else bload16_lds(vrs, vbuf + 1024 * (4 * (i - 4) + wave), v_lane, (uint32_t)(16 * (i - 4)) * vss_s);
   }
+  // Segment-constant addressing with the tile offsets given: DMA i of a K tile
+  // (i < 4, offset kto) or of a V tile (i >= 4, offset vto), so that one step
+  // can load K and V of different tiles
+  __device__ __forceinline__ void issue_at(int i, char* kbuf, char* vbuf, uint32_t kto, uint32_t vto) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (i < 4) bload16_lds(krs_seg, kbuf + 1024 * (4 * i + wave), ko[i], kto);
+    else bload16_lds(vrs_seg, vbuf + 1024 * (4 * (i - 4) + wave), vo[i - 4], vto);
+  }
   // after this wave's DMAs into kbuf and vbuf have landed (vmcnt): zero the
   // V rows (and with K, the K rows) it loaded past the sequence end; every
   // lane clears the 16 bytes it wrote (K load i holds rows 16 i + lane % 16,
-  // see issue)
+  // see issue).  nvalid: the tile's valid keys (default: the prepared tile's)
   template <bool K>
-  __device__ __forceinline__ void zero_tail(char* kbuf, char* vbuf) {
-    if (pnvalid >= kUnitKeys) return;                     // uniform: only a sequence's last tile
+  __device__ __forceinline__ void zero_tail(char* kbuf, char* vbuf) { zero_tail_n<K>(kbuf, vbuf, pnvalid); }
+  template <bool K>
+  __device__ __forceinline__ void zero_tail_n(char* kbuf, char* vbuf, int nvalid) {
+    if (nvalid >= kUnitKeys) return;                      // uniform: only a sequence's last tile
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (K && k_row0 + 16 * i >= pnvalid)
+      if (K && k_row0 + 16 * i >= nvalid)
         *reinterpret_cast<u32x4*>(kbuf + 1024 * (4 * i + wave) + 16 * lane) = u32x4{0, 0, 0, 0};
-      if (v_row0 + 16 * i >= pnvalid)
+      if (v_row0 + 16 * i >= nvalid)
         *reinterpret_cast<u32x4*>(vbuf + 1024 * (4 * i + wave) + 16 * lane) = u32x4{0, 0, 0, 0};
     }
   }
@@ -2043,6 +2060,11 @@ struct DirectStage {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A workgroup barrier for LDS only: this wave's LDS writes complete, then the
+// barrier, with no wait on vector memory (the fence of __syncthreads would
+// drain every DMA still in flight).  The LDS DMAs a barrier must cover are
+// waited for explicitly before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -2082,6 +2104,15 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   constexpr bool DKF8 = KIND == KIND_F8 && D == 128 && FAST;
   // PV operands by transpose reads from a row-major bf16 V stage
   constexpr bool TRV = DIRECT || DKF8;
+  // The lean bf16 build keeps three K stages and two V stages: a step issues
+  // the next tile's V (first) and the K of the tile after it, so both have
+  // more than a tile of QK, softmax and PV to land (the V DMAs go out in the
+  // first half of the QK loop).  The K stage rotates at run time (one base
+  // per tile for its reads); the V stage alternates with the step's parity.
+  constexpr bool K3 = LEAN && DIRECT;
+  int ks = 0;                         // K3: the current tile's K stage
+  uint32_t vt_next = 0;               // K3: V offset of the tile after the current one
+  int nv_next = kUnitKeys;            //      and its valid keys
   char* const v8buf = smem + 2 * C::K_TILE;         // DKF8: fp8 V staging (single)
   // Row sums of P stay on the VALU in fp32: an MFMA sum of the bf16 P operand
   // carries its rounding (up to 2^-9 on the largest term, which under the lazy
@@ -2164,7 +2195,19 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
     auto tile_of = [&](int u) {   // wave-uniform: keeps tile addressing in scalar registers
       return __builtin_amdgcn_readfirstlane(tp.has_bm ? (int)list[u - c0] : t_lo + u);
     };
-    if constexpr (DIRECT) {
+    if constexpr (K3) {
+      // tile c0's K and V, landed and tail-zeroed; then the K of tile c0 + 1
+      // goes out and its V offsets are kept for the first step
+      ks = 0;
+      ds.load<LEAN>(p, s, tile_of(c0), smem, vstage<true>(0));
+      wait_vmem();
+      ds.zero_tail<true>(smem, vstage<true>(0));
+      ds.prep<LEAN>(p, s, tile_of(min(c0 + 1, c0 + cn - 1)));
+      vt_next = ds.vtoff;
+      nv_next = ds.pnvalid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds.issue_at(i, smem + C::K_TILE, nullptr, ds.ktoff, 0);
+    } else if constexpr (DIRECT) {
       ds.load<LEAN>(p, s, tile_of(c0), smem, vstage<true>(0));
       wait_vmem();
       ds.zero_tail<LEAN>(smem, vstage<true>(0));
@@ -2184,16 +2227,20 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       cur_ksc = stg.ksc;
       cur_vsc = stg.vsc;
     }
-    __syncthreads();
+    if constexpr (K3) lds_barrier();
+    else __syncthreads();
     // one tile; BUF (a compile-time 0 / 1) selects the stage it reads, so every
     // LDS address is a lane register plus an immediate offset
     auto step = [&](int u, auto buf_c) {
       constexpr int buf = decltype(buf_c)::value;
-      char* kbuf = TRV ? smem + buf * C::K_TILE : smem + buf * C::STAGE;
+      char* kbuf = K3 ? smem + ks * C::K_TILE : TRV ? smem + buf * C::K_TILE : smem + buf * C::STAGE;
       char* vbuf = kbuf + C::K_TILE;
       const bool more = u + 1 < c0 + cn;
-      char* nkb = smem + (buf ^ 1) * C::K_TILE;
+      const int ks2 = ks == 0 ? 2 : ks - 1;             // K3: the stage two tiles ahead ((ks + 2) % 3)
+      char* nkb = K3 ? smem + ks2 * C::K_TILE : smem + (buf ^ 1) * C::K_TILE;
       char* nvb = nullptr;
+      uint32_t vt1 = 0, kt2 = 0;                       // K3: V offset of tile u + 1, K offset of tile u + 2
+      int nv1 = kUnitKeys;
       float nksc = 1.f, nvsc = 1.f;                    // DKF8: scales of the next tile
       if constexpr (DKF8) {
         // the next tile's K and V go out before the QK MFMAs (a chunk's last
@@ -2205,6 +2252,21 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         ds.issue_v8<LEAN>(0, v8buf);
         ds.issue_v8<LEAN>(1, v8buf);
         nksc = kscale_at_page<KIND>(p, s, ds.ppage, &nvsc);
+      } else if constexpr (K3) {
+        // the V of tile u + 1 and the K of tile u + 2 go out between the QK
+        // MFMAs below, V first (past the chunk's end a step re-loads its
+        // last tile into an idle stage)
+        nvb = vstage<true>(buf ^ 1);
+        vt1 = vt_next;
+        nv1 = nv_next;
+        ds.prep<LEAN>(p, s, tile_of(min(u + 2, c0 + cn - 1)));
+        kt2 = ds.ktoff;
+        vt_next = ds.vtoff;
+        nv_next = ds.pnvalid;
+        if (!wave_live) {                               // a wave with no rows still loads its share
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ds.issue_at(i < 4 ? 4 + i : i - 4, nkb, nvb, kt2, vt1);
+        }
       } else if constexpr (DIRECT) {
         // the next tile's DMAs go out between the QK MFMAs below (the last
         // step of a chunk re-loads its own tile into the idle stage)
@@ -2331,7 +2393,11 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
                 const int mb = i % 4, ks = i / 4;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) sc[nb][mb] = mfma_qk(ka, qB[nb][ks], LEAN && ks == 0 ? init(nb, mb) : sc[nb][mb]);
-                if constexpr (DIRECT) { if (i % 2 == 1) ds.issue<LEAN>(i / 2, nkb, nvb); }
+                if constexpr (K3) {
+                  if (i % 2 == 1) ds.issue_at(i / 2 < 4 ? 4 + i / 2 : i / 2 - 4, nkb, nvb, kt2, vt1);
+                } else if constexpr (DIRECT) {
+                  if (i % 2 == 1) ds.issue<LEAN>(i / 2, nkb, nvb);
+                }
                 __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
                 if (i + KDEP < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 if constexpr (DIRECT) { if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); }
@@ -2456,7 +2522,13 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (DIRECT) {
+      if constexpr (K3) {
+        // tile u + 1's K (issued a step ago) and V (this step) have landed;
+        // the four K DMAs of tile u + 2, issued last, may still be in flight
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        ks = ks == 2 ? 0 : ks + 1;
+        ds.zero_tail_n<true>(smem + ks * C::K_TILE, nvb, nv1);
+      } else if constexpr (DIRECT) {
         wait_vmem();
         ds.zero_tail<LEAN>(nkb, nvb);
       } else if constexpr (DKF8) {
@@ -2471,12 +2543,16 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         cur_ksc = stg.ksc;
         cur_vsc = stg.vsc;
       }
-      __syncthreads();
+      if constexpr (K3) lds_barrier();
+      else __syncthreads();
     };
     for (int u = c0; u < c0 + cn; u += 2) {
       step(u, std::integral_constant<int, 0>{});
       if (u + 1 < c0 + cn) step(u + 1, std::integral_constant<int, 1>{});
     }
+    // K3: the last step's K DMAs (into an idle stage) land before the stages
+    // are reused (the next chunk, or the fused merge's slots)
+    if constexpr (K3) wait_vmem();
   }
 
   // epilogue: per lane row, reduce l over the four lane groups and write
@@ -2643,7 +2719,7 @@ __global__ __launch_bounds__(kThreads, (Lds<KIND, D, FAST>::OCC)) void attention
 // succeeded, and concurrent first calls merely repeat the idempotent set.
 template <int KIND, int D, bool FAST, int PATHS>
 static hipError_t launch_attention_t(const KParams& p, int grid, hipStream_t stream) {
-  const int lds = Lds<KIND, D, FAST>::DYN;
+  const int lds = PATHS == kPathsLean ? Lds<KIND, D, FAST>::DYN_LEAN : Lds<KIND, D, FAST>::DYN;
   static std::atomic<uint64_t> configured{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
