@@ -143,8 +143,10 @@ def test_device_info():
     lambda: W.splitk_decode(q_len=[1, 2, 4, 3] * 4, batch=16, ctx_lo=64, ctx_hi=3000),
     lambda: W.hybrid_chunked(batch=12, chunk=200, history=700, dec_lo=100, dec_hi=2000),
     lambda: W.sparse_prefill(kind="bf16", seq_len=1024),
+    lambda: W.sparse_prefill(kind="bf16", seq_len=1000, mask=False),
+    lambda: W.sparse_prefill(kind="e4m3", seq_len=1000, mask=False),
     lambda: W.sliding_window(seq_len=1500, window=512),
-], ids=["tiny", "decode", "mtp_mix", "hybrid", "sparse", "window"])
+], ids=["tiny", "decode", "mtp_mix", "hybrid", "sparse", "dense_lean", "dense_lean_fp8", "window"])
 @pytest.mark.parametrize("workers,force,weight", [(0, 0, 0), (0, 0, 73), (7, 0, 0), (64, 0, 35), (37, 1, 0),
                                                   (5, 3, 90)])
 def test_taskmap_bit_exact(make, workers, force, weight):
