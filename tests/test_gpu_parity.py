@@ -542,6 +542,23 @@ def test_large_qblocks_ragged_tails_poisoned(kind, mode):
     compare(b, out, lse)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "e4m3"])
+def test_large_qblock_segment_over_one_tile_chunk(kind):
+    """A worker segment longer than the 1024-tile chunk the large-Q-block loop
+    takes at once (forced split of 4096 units per worker over a 70,000-key
+    context): the K/V pipeline restarts at the chunk boundary, and the result
+    still matches the oracle (sampled rows)."""
+    rng = np.random.default_rng(33)
+    b = W.build_batch(rng, name=f"long_segment_{kind}", kind=kind, Hq=32, Hkv=8, d=128, page_size=64,
+                      ctx=[70000], q_len=[32], quant_mode="tensor" if kind == "e4m3" else None)
+    P = B.paged_attn_device_info(0)["default_workers"]
+    force = 4096
+    g, out, lse, ws = gpu_run(b, force_split_units=force, max_partial_slots=slots_for(b, P, force))
+    h = check_no_device_error(ws, g, force_split_units=force, max_partial_slots=slots_for(b, P, force))
+    assert h[2] == force
+    compare(b, out, lse, rows=sample_rows(b.total_q, 12, must=(0, 31)))
+
+
 def test_sliding_window_ragged_tail_poisoned():
     """The sliding-window forward (landmarks every 64 keys: the lean build)
     over a sequence that ends inside a tile, its pages' free slots poisoned."""
