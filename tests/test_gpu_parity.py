@@ -573,11 +573,15 @@ def test_sliding_window_ragged_tail_poisoned():
     (lambda: W.splitk_decode(q_len=[1, 2, 4, 3] * 4, batch=16, ctx_lo=64, ctx_hi=6000), {"max_q_len": 0}),
     (lambda: W.hybrid_chunked(batch=12, chunk=300, history=900, dec_lo=100, dec_hi=3000), {}),
     (lambda: W.sparse_prefill(kind="e4m3", seq_len=1024), {"force_split_units": 3}),
+    (lambda: W.sparse_prefill(kind="bf16", seq_len=1000, mask=False), {"force_split_units": 3}),
+    (lambda: W.sparse_prefill(kind="e4m3", seq_len=1000, mask=False), {"force_split_units": 5}),
+    (lambda: W.sliding_window(seq_len=1500, window=512), {"force_split_units": 4}),
     (lambda: W.sliding_window(decode=True), {"split": "static", "static_splits": 8}),
     (lambda: W.build_batch(np.random.default_rng(8), name="empty_qblocks", kind="bf16", Hq=8, Hkv=2, d=64,
                            page_size=16, ctx=[40, 300, 90], q_len=[3, 300, 2], num_pages=40, window=1,
                            landmark_chunk=2, window_expand_to_chunk=False), {}),
-], ids=["decode", "mtp_general", "hybrid", "fp8_forced", "static", "empty"])
+], ids=["decode", "mtp_general", "hybrid", "fp8_forced", "lean_bf16_forced", "lean_fp8_forced", "lean_window_forced",
+        "static", "empty"])
 def test_fused_combine_equals_combine_kernel(make, kw):
     """The fused merge (last finisher of a split Q-block) runs the same
     arithmetic in the same order as the Combine kernel: bit-identical."""
