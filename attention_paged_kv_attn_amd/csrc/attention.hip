@@ -2110,6 +2110,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
   // first half of the QK loop).  The K stage rotates at run time (one base
   // per tile for its reads); the V stage alternates with the step's parity.
   constexpr bool K3 = LEAN && DIRECT;
+  // The lean fp8 build widens a tile's V at the start of its own step (the
+  // conversions run beside the QK MFMAs), with an LDS barrier before PV
+  // instead of the widening at the end of the previous step.
+  constexpr bool WD = LEAN && DKF8;
   int ks = 0;                         // K3: the current tile's K stage
   uint32_t vt_next = 0;               // K3: V offset of the tile after the current one
   int nv_next = kUnitKeys;            //      and its valid keys
@@ -2220,7 +2224,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       cur_ksc = kscale_at_page<KIND>(p, s, ds.ppage, &cur_vsc);
       wait_vmem();
       if constexpr (LEAN) ds.zero_tail_k8(smem);
-      ds.widen_v8(v8buf, vstage<true>(0));
+      if constexpr (!WD) ds.widen_v8(v8buf, vstage<true>(0));
     } else {
       stg.load(p, s, tile_of(c0), FAST ? ds.page_of_tile(p, tile_of(c0) * kUnitKeys) : -1);
       stg.store(smem, smem + C::K_TILE);
@@ -2243,6 +2247,13 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       int nv1 = kUnitKeys;
       float nksc = 1.f, nvsc = 1.f;                    // DKF8: scales of the next tile
       if constexpr (DKF8) {
+        if constexpr (WD) {
+          // this tile's V (landed at the end of the previous step) to bf16
+          // into its V stage; the staging block's reads complete before the
+          // next tile's V DMAs below may write it
+          ds.widen_v8(v8buf, vstage<true>(buf));
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
         // the next tile's K and V go out before the QK MFMAs (a chunk's last
         // step re-loads its own tile into the idle stage, as the bf16 path)
         nvb = vstage<true>(buf ^ 1);
@@ -2452,6 +2463,9 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
         for (int nb = 0; nb < NB; ++nb)
           softmax_update<KIND, D, NB, !MSUM>(st, nb, sc[nb], KIND == KIND_F8 ? cs * rm[nb].qs : cs);
         __builtin_amdgcn_s_setprio(0);
+        // WD: every wave's widened V rows are in LDS before any PV read (a
+        // wave with no rows takes its barrier in the else branch below)
+        if constexpr (WD) lds_barrier();
         // O^T += V^T P^T
         if constexpr (KIND == KIND_F32) {
 #pragma unroll
@@ -2520,6 +2534,8 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
             }
           }
         }
+      } else {
+        if constexpr (WD) lds_barrier();
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (K3) {
@@ -2534,7 +2550,7 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
       } else if constexpr (DKF8) {
         wait_vmem();                                     // this wave's K and V DMAs have landed
         if constexpr (LEAN) ds.zero_tail_k8(nkb);
-        ds.widen_v8(v8buf, nvb);
+        if constexpr (!WD) ds.widen_v8(v8buf, nvb);
         cur_ksc = nksc;
         cur_vsc = nvsc;
       } else if (more) {
