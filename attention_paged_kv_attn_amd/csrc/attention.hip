@@ -273,6 +273,10 @@ __device__ __forceinline__ u32x4 gload16(const char* base, uint32_t voff, uint32
 __device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL u32x2*)(base + soff + voff);
 }
+// temporal 16-byte load: fp8 K rows read in two halves by consecutive loads
+__device__ __forceinline__ u32x4 gload16t(const char* base, uint32_t voff, uint32_t soff) {
+  return *(const PA_GLOBAL u32x4*)(base + soff + voff);
+}
 __device__ __forceinline__ unsigned gload4(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL unsigned*)(base + soff + voff);
 }
@@ -393,15 +397,31 @@ __device__ __forceinline__ float kscale_of(const KParams& p, const SeqCtx& s, in
 // QK operands of lane group h from a row: K-step ks holds dims 32 ks + 8 h ..+7
 // (bf16, fp8) or 16 (ks / 4) + 4 h + ks % 4 (fp32).  `at` points at the row's
 // dim 8 h (bf16, fp8) or 4 h (fp32) already; nullptr loads zeros.
+//
+// PAIRED (fp8 only): K-steps 2c and 2c + 1 hold dims 64 c + 16 h ..+7 and
+// ..+8 ..+15, so that a lane reads 16 contiguous bytes per pair of K-steps.
+// The dot product over d does not depend on which dims meet in a K-step, so Q
+// and K only have to agree: the sequence-Q-block path loads both this way
+// (measured 1-2% faster for fp8 decode on MI355X); the other small paths
+// (measured 2.5% slower with it) and the large path keep the plain order.
 template <int KIND>
+constexpr bool kPairedK = KIND == KIND_F8;
+template <int KIND, bool PAIRED = false>
 __device__ __forceinline__ int lane_dim_bytes(int h) {
-  return KIND == KIND_F32 ? 16 * h : (KIND == KIND_BF16 ? 16 * h : 8 * h);
+  return KIND == KIND_F32 ? 16 * h : (KIND == KIND_BF16 || PAIRED ? 16 * h : 8 * h);
 }
 
-template <int KIND, int D>
+template <int KIND, int D, bool PAIRED = false>
 __device__ __forceinline__ void load_qk_at(const char* at, typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
   using C = Cfg<KIND, D>;
-  if constexpr (KIND == KIND_BF16) {
+  if constexpr (KIND == KIND_F8 && PAIRED) {
+#pragma unroll
+    for (int c = 0; c < C::KSQ / 2; ++c) {
+      const u32x4 v = at ? *reinterpret_cast<const u32x4*>(at + 64 * c) : u32x4{0, 0, 0, 0};
+      op[2 * c] = __builtin_bit_cast(long, u32x2{v[0], v[1]});
+      op[2 * c + 1] = __builtin_bit_cast(long, u32x2{v[2], v[3]});
+    }
+  } else if constexpr (KIND == KIND_BF16) {
 #pragma unroll
     for (int ks = 0; ks < C::KSQ; ++ks) {
       u32x4 v = at ? *reinterpret_cast<const u32x4*>(at + 64 * ks) : u32x4{0, 0, 0, 0};
@@ -420,10 +440,10 @@ __device__ __forceinline__ void load_qk_at(const char* at, typename QKOpT<KIND>:
   }
 }
 
-template <int KIND, int D>
+template <int KIND, int D, bool PAIRED = false>
 __device__ __forceinline__ void load_qk_row(const char* row, int h,
                                             typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
-  load_qk_at<KIND, D>(row ? row + lane_dim_bytes<KIND>(h) : nullptr, op);
+  load_qk_at<KIND, D, PAIRED>(row ? row + lane_dim_bytes<KIND, PAIRED>(h) : nullptr, op);
 }
 
 // ---------------------------------------------------------------------------
@@ -775,11 +795,18 @@ struct SmallRegs {
 };
 
 // QK operands from a buffer: K-step ks of lane group h at voff + (ks part), soff.
-template <int KIND, int D>
+template <int KIND, int D, bool PAIRED = false>
 __device__ __forceinline__ void bload_qk(const char* r, uint32_t voff, uint32_t soff,
                                          typename QKOpT<KIND>::T (&op)[Cfg<KIND, D>::KSQ]) {
   using C = Cfg<KIND, D>;
-  if constexpr (KIND == KIND_BF16) {
+  if constexpr (KIND == KIND_F8 && PAIRED) {
+#pragma unroll
+    for (int c = 0; c < C::KSQ / 2; ++c) {
+      const u32x4 v = gload16t(r, voff + 64 * c, soff);
+      op[2 * c] = __builtin_bit_cast(long, u32x2{v[0], v[1]});
+      op[2 * c + 1] = __builtin_bit_cast(long, u32x2{v[2], v[3]});
+    }
+  } else if constexpr (KIND == KIND_BF16) {
 #pragma unroll
     for (int ks = 0; ks < C::KSQ; ++ks) op[ks] = __builtin_bit_cast(bf16x8, gload16(r, voff + 64 * ks, soff));
   } else if constexpr (KIND == KIND_F8) {
@@ -803,7 +830,7 @@ __device__ __forceinline__ typename VRawT<KIND, MD>::T bload_v(const char* r, ui
   else return gload4(r, voff, soff);
 }
 
-template <int KIND, int D, bool FAST>
+template <int KIND, int D, bool FAST, bool PAIRED = false>
 __device__ __forceinline__ void small_load_k(const KParams& p, const SeqCtx& s, const Tile<Cfg<KIND, D>::ELT, FAST>& t,
                                              SmallRegs<KIND, D>& r, int n, int h) {
   if constexpr (FAST) {
@@ -811,12 +838,12 @@ __device__ __forceinline__ void small_load_k(const KParams& p, const SeqCtx& s, 
     // cache memory: read them unclamped (their scores are masked to -inf by
     // select, never used).  Uniform row bases + one lane offset keep every
     // load in the scalar-base form.
-    const uint32_t lane = (uint32_t)n * t.kss + lane_dim_bytes<KIND>(h);
+    const uint32_t lane = (uint32_t)n * t.kss + lane_dim_bytes<KIND, PAIRED>(h);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) bload_qk<KIND, D>(t.kb + 16 * mb * t.kss, lane, 0u, r.kA[mb]);
+    for (int mb = 0; mb < 4; ++mb) bload_qk<KIND, D, PAIRED>(t.kb + 16 * mb * t.kss, lane, 0u, r.kA[mb]);
   } else {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) load_qk_row<KIND, D>(t.krow(p, s, 16 * mb + n), h, r.kA[mb]);
+    for (int mb = 0; mb < 4; ++mb) load_qk_row<KIND, D, PAIRED>(t.krow(p, s, 16 * mb + n), h, r.kA[mb]);
   }
 }
 
@@ -1522,8 +1549,6 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
 // (the output, or its rows of the worker's partial slot), so no wave merges
 // with another.
 // ---------------------------------------------------------------------------
-template <int KIND>
-constexpr bool kHeadsHalfStep = true;
 
 template <int KIND, int D, bool FAST>
 __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap wm, int a, int b) {
@@ -1547,8 +1572,8 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
     const int tok = x.q0 + (row_ok ? ti : 0), head = wave * wr + jr;
     const int rkv = head / p.G;
     typename QKOpT<KIND>::T qB[C::KSQ];
-    load_qk_row<KIND, D>(row_ok ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
-                                : nullptr, h, qB);
+    load_qk_row<KIND, D, kPairedK<KIND>>(row_ok ? reinterpret_cast<const char*>(p.q) + (tok * p.q_st + head * p.q_sh) * C::ELT
+                                               : nullptr, h, qB);
     RowMask rm;
     rm.pos = x.ctx - x.ql + (row_ok ? ti : 0);
     rm.left = p.window > 0 ? window_left(p, rm.pos) : 0;
@@ -1610,30 +1635,24 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
     SmallRegs<KIND, D> r;
     // lane offsets from an opaque copy of the thread id (rebuilt per tile, not spilled)
     auto lane_n = [&]() { int tid = threadIdx.x; asm volatile("" : "+v"(tid)); return tid; };
-    if constexpr (!kHeadsHalfStep<KIND>) {
-      // one tile in flight per wave: the second wave on each SIMD computes
-      // while this one waits
-      for (; k0 < hi; advance(k0, jj)) {
-        prepare(tc, sc_, k0, jj);
-        const int tid = lane_n();
-        small_load_k<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
-        small_load_v<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
-        rm.bit = row_ok && rkv == sc_.g;                 // only this kv head's rows see the tile
-        f32x4 sc[4];
-        const float vsc = small_scores<KIND, D, FAST>(p, sc_, x, tc, r, QFromRegs<KIND, D>{qB}, rm, 0, pos_min,
-                                                       left_max, st, lane, sc, mixed);
-        small_pv<KIND, D>(r, sc, vsc, st);
-      }
-    } else if (k0 < hi) {
+    // The next unit's K goes out once this unit's QK has read K, and its V
+    // once this unit's PV has read V.  The next QK waits for both: the
+    // compiler's wait analysis also follows paths of this control flow that
+    // never run (the loop entered without the first tile's loads, K loaded
+    // and V not) and so waits for nearly every load in flight there.  Only K
+    // is needed, but the exact wait (V left in flight through the QK and the
+    // softmax, one more tile's loads outstanding per wave; built with a loop
+    // that no such path reaches) measured 2-4% slower on MI355X for bf16 and
+    // fp8 decode, and an explicit full wait ahead of the tile's scale loads
+    // 1.5% slower for fp8: the memory system does better with fewer requests
+    // in flight here, and the second wave on each SIMD covers the wait.
+    if (k0 < hi) {
       prepare(tc, sc_, k0, jj);
       const int tid = lane_n();
-      small_load_k<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
+      small_load_k<KIND, D, FAST, kPairedK<KIND>>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
       small_load_v<KIND, D, FAST>(p, sc_, tc, r, tid & 15, (tid >> 4) & 3);
     }
-    // half a tile ahead: the next unit's K goes out once this unit's QK has
-    // read K, its V once this unit's PV has read V, so a wave keeps loads in
-    // flight through its own compute without a second tile of registers
-    while (kHeadsHalfStep<KIND> && k0 < hi) {
+    while (k0 < hi) {
       int nk0 = k0, nj = jj;
       advance(nk0, nj);
       const bool more = nk0 < hi;
@@ -1644,7 +1663,7 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
       if (more) {
         prepare(tn, sn, nk0, nj);
         const int tid = lane_n();
-        small_load_k<KIND, D, FAST>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
+        small_load_k<KIND, D, FAST, kPairedK<KIND>>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
       }
       small_pv<KIND, D>(r, sc, vsc, st);
       if (more) {
