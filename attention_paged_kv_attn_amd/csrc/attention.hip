@@ -370,6 +370,24 @@ __device__ __forceinline__ float kscale_at_page(const KParams& p, const SeqCtx& 
   }
 }
 
+// fp8 K and V scales read once by a caller that runs many tiles, in
+// per-tensor mode.  `valid` is false for per-(page, head) scales, which stay
+// a per-tile load, and for bf16 and fp32 (scales of 1, no load).  Without it
+// the two scale loads of every tile sit between the tile's K/V loads and its
+// softmax, which then waits for them as well.
+struct KvScales {
+  float k, v;
+  bool valid;
+};
+template <int KIND>
+__device__ __forceinline__ KvScales kv_scales_hoisted(const KParams& p) {
+  if constexpr (KIND != KIND_F8) return KvScales{1.f, 1.f, false};
+  else {
+    if ((p.scale_mode & 3) == 2) return KvScales{1.f, 1.f, false};
+    return KvScales{p.k_scale[0], p.v_scale[0], true};
+  }
+}
+
 // Q scale of one query row: per tensor, or per (query token, query head)
 // from a [total_q, Hq] array.
 template <int KIND>
@@ -951,14 +969,20 @@ __device__ __forceinline__ float small_scores(const KParams& p, const SeqCtx& s,
                                               const Tile<Cfg<KIND, D>::ELT, FAST>& tc, const SmallRegs<KIND, D>& r,
                                               const QSrc& qsrc, RowMask& rm, int bm_head, int pos_min, int left_max,
                                               WaveState<KIND, D, 1>& st, int lane, f32x4 (&sc)[4],
-                                              bool rows_mixed = false) {
+                                              bool rows_mixed = false, KvScales ts = KvScales{1.f, 1.f, false}) {
   using C = Cfg<KIND, D>;
   const int h = lane >> 4;
   const int J0 = tc.J0;
   float vsc;
   float ksc;
-  if constexpr (FAST) ksc = kscale_at_page<KIND>(p, s, tc.page, &vsc);
-  else ksc = kscale_of<KIND>(p, s, J0, &vsc);
+  if (KIND == KIND_F8 && ts.valid) {
+    ksc = ts.k;
+    vsc = ts.v;
+  } else if constexpr (FAST) {
+    ksc = kscale_at_page<KIND>(p, s, tc.page, &vsc);
+  } else {
+    ksc = kscale_of<KIND>(p, s, J0, &vsc);
+  }
   if (p.bm) {
     const int kt = J0 / p.bm_tile, qt = rm.pos / p.bm_tile;
     rm.bit = kt < p.bm_nk && qt < p.bm_nq &&
@@ -1381,6 +1405,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
   const int wa = wave_uniform(a + (cnt * wave) / kWaves), wb = wave_uniform(a + (cnt * (wave + 1)) / kWaves);
 
   if (wa < wb) {
+    const KvScales ts = kv_scales_hoisted<KIND>(p);
     // the current piece: its Q-block, state and row mask
     int cur_q = -1;
     QBlock cx;
@@ -1427,7 +1452,7 @@ __device__ PA_SEGMENT_FN void small_range(uint64_t pk, int vw, const WorkerMap w
       }
       SeqCtx s{cx.b, cx.g, cx.ctx, rec.t_lo, p.bt + (int64_t)cx.b * p.bt_stride};
       return small_scores<KIND, D, FAST>(p, s, cx, rec.t, rec.r, QFromRegs<KIND, D>{rec.qB}, rm, 0, pos_min,
-                                         left_max, st, lane, sc);
+                                         left_max, st, lane, sc, false, ts);
     };
     // the Q-block of the first unit
     StreamCursor c;
@@ -1559,6 +1584,7 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
   const int Hkv = wave_uniform(p.Hkv), hpw = Hkv >> 2, wr = hpw * p.G;
   const bool mixed = hpw > 1;
   const int n_qb = p.hdr[H_NQB];
+  const KvScales ts = kv_scales_hoisted<KIND>(p);
   int pbase = -(1 << 30), vpage = 0, cur_b = -1;
   for (int q = find_qblock(p, 0, n_qb - 1, a, lane); q < n_qb; ++q) {
     const int S = wave_uniform(p.unit_prefix[q]), E = wave_uniform(p.unit_prefix[q + 1]);
@@ -1659,7 +1685,7 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
       rm.bit = row_ok && rkv == sc_.g;                   // only this kv head's rows see the tile
       f32x4 sc[4];
       const float vsc = small_scores<KIND, D, FAST>(p, sc_, x, tc, r, QFromRegs<KIND, D>{qB}, rm, 0, pos_min,
-                                                     left_max, st, lane, sc, mixed);
+                                                     left_max, st, lane, sc, mixed, ts);
       if (more) {
         prepare(tn, sn, nk0, nj);
         const int tid = lane_n();
