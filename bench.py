@@ -166,6 +166,31 @@ FLUSH_BYTES = 1 << 30
 FLUSH_BELOW_BYTES = 1_000_000_000
 
 
+# Warm-up: the W untimed steps, then more until the leg's step has run
+# back to back for this long.  A leg starts after seconds of host-side input
+# generation with the GPU idle; its first ~50 ms of steps measured 5-15%
+# slower on MI355X (prefill 1.04-1.09 ms against 0.98-1.00 ms once warm).
+MIN_WARMUP_S = 0.25
+
+
+def warm_up(run, warmup):
+    """Runs `run` warmup times, then in batches of 8 until MIN_WARMUP_S of
+    wall time has passed; returns the number of calls."""
+    import torch
+    n = 0
+    for _ in range(warmup):
+        run()
+        n += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(8):
+            run()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def flush_caches():
     """Read a 1 GiB scratch buffer: evicts the L2s and the 256 MiB MALL with
     clean lines, so a working set under 1 GB is read from HBM on every timed
@@ -190,9 +215,7 @@ def time_graph(g, kw, steps, warmup, leg_name):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
+    n_warm = warm_up(graph.replay, warmup)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -200,7 +223,7 @@ def time_graph(g, kw, steps, warmup, leg_name):
         graph.replay()
     t1.record()
     torch.cuda.synchronize()
-    LAUNCH_LOG.append((leg_name, 1 + 2 * warmup + steps, steps))
+    LAUNCH_LOG.append((leg_name, 1 + warmup + n_warm + steps, steps))
     return t0.elapsed_time(t1) / steps
 
 
@@ -218,9 +241,7 @@ def time_workload(batch, steps, warmup, split=None, flush=False, leg_name=None, 
     kw = split_kw(split, g)
     out, lse, ws = B.run_batch(g, **kw)      # allocates outputs + workspace once
     torch.cuda.synchronize()
-    for _ in range(warmup):
-        B.run_batch(g, out=out, lse=lse, workspace=ws, **kw)
-    torch.cuda.synchronize()
+    n_warm = warm_up(lambda: B.run_batch(g, out=out, lse=lse, workspace=ws, **kw), warmup)
     B.paged_attn_kernel_timing_read()         # clear
     B.paged_attn_kernel_timing(True)
     stream = torch.cuda.current_stream()
@@ -243,7 +264,7 @@ def time_workload(batch, steps, warmup, split=None, flush=False, leg_name=None, 
         ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
     else:
         ms = ev[0][0].elapsed_time(ev[-1][1]) / steps
-    LAUNCH_LOG.append((leg_name, 1 + warmup + steps, steps))
+    LAUNCH_LOG.append((leg_name, 1 + n_warm + steps, steps))
     return ms, {"assign": a / n, "attention": att / n, "combine": c / n}, flush
 
 
@@ -603,7 +624,11 @@ def summarize_profiles(d):
 
 
 def profile_leg(name, steps, warmup):
-    """One workload only (for counter runs): prints its timing as JSON."""
+    """One workload only (for counter runs, which count every dispatch: the
+    timed-warm-up is off so that the W warm-up steps and the timed ones are
+    all there is): prints its timing as JSON."""
+    global MIN_WARMUP_S
+    MIN_WARMUP_S = 0.0
     batch, by, flops, ms, kms, flushed = leg(name, steps, warmup)
     print(json.dumps({"workload": name, "ms_per_step": ms, "kernels_ms": kms}), flush=True)
 
@@ -612,7 +637,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps per leg (then more, back to back, until MIN_WARMUP_S has passed)")
     ap.add_argument("--workload", default="splitk_decode_q1_NHD", choices=sorted(WORKLOADS))
     ap.add_argument("--prefill-workload", default="prefill_bf16_dense", choices=sorted(WORKLOADS) + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -642,6 +668,12 @@ def main():
         profile_leg(args.profile_leg, args.steps, args.warmup)
         return
 
+    # the flush buffer is allocated and read once before any leg: the steps
+    # that followed its first allocation measured 8-15% slower for tens of
+    # milliseconds (bf16 prefill 1.05-1.14 ms against 0.98 ms), which landed
+    # on the first flushed leg
+    flush_caches()
+    torch.cuda.synchronize()
     batch, by, flops, ms, kms, flushed = leg(args.workload, args.steps, args.warmup)
     gbs = by / (ms * 1e-3) / 1e9
     dtype = {"f32": "f32", "bf16": "bf16", "e4m3": "fp8"}[batch.kind]
@@ -654,6 +686,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_note": f"per leg: {args.warmup} steps, then back to back until {MIN_WARMUP_S} s",
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
