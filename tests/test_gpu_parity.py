@@ -674,6 +674,32 @@ def test_fp8_small_pages(d):
     compare(b, out, lse)
 
 
+@pytest.mark.parametrize("kind,d,page_size,layout,quant,Hq,Hkv,qmax", [
+    ("e4m3", 64, 64, "NHD", "tensor", 16, 4, 4),
+    ("e4m3", 64, 64, "HND", "page_head", 32, 8, 2),
+    ("e4m3", 64, 16, "NHD", "tensor", 16, 4, 3),
+    ("e4m3", 128, 16, "HND", "tensor", 32, 8, 2),
+    ("bf16", 64, 64, "NHD", None, 16, 4, 4),
+    ("bf16", 64, 16, "HND", None, 32, 8, 1),
+])
+def test_sequence_qblocks_head_dims_and_pages(kind, d, page_size, layout, quant, Hq, Hkv, qmax):
+    """Decode with sequence Q-blocks (every query head of a sequence in one
+    block) at d = 64 and with 16-token pages, where the fp8 K rows and Q rows
+    are read in the paired dim order (two K-steps per 16-byte read) through
+    both the page-window and the per-key row lookups; ragged contexts end
+    mid-tile."""
+    rng = np.random.default_rng(300 + d + page_size + Hkv)
+    nb = 10
+    ctx = rng.integers(40, 3000, size=nb)
+    q_len = rng.integers(1, qmax + 1, size=nb)
+    b = W.build_batch(rng, name=f"seqqb_{kind}_d{d}_p{page_size}_{layout}", kind=kind, Hq=Hq, Hkv=Hkv, d=d,
+                      page_size=page_size, ctx=ctx, q_len=q_len, kv_layout=layout, quant_mode=quant,
+                      q_quant="token_head" if kind == "e4m3" else "tensor")
+    g, out, lse, ws = gpu_run(b)
+    check_no_device_error(ws, g)
+    compare(b, out, lse)
+
+
 def test_auto_policy_runs_each_shape():
     for b in (W.splitk_decode(q_len=1, batch=12, ctx_lo=100, ctx_hi=6000),
               W.build_batch(np.random.default_rng(5), name="uniform", kind="bf16", Hq=32, Hkv=8, d=128,
