@@ -2528,9 +2528,10 @@ __device__ PA_SEGMENT_FN void large_segment(uint64_t pk, const QBlock x, int t_l
               }
         } else if constexpr (TRV) {
           // V^T operands by transpose reads, VDEP operands ahead of their MFMAs
-          // (twelve in the lean fp8 build, measured 3.5% faster there; the
-          // general builds spill with twelve)
-          constexpr int NV = 2 * MD, VDEP = KIND == KIND_F8 && LEAN ? 12 : 8;
+          // (ten in the lean fp8 build: measured on MI355X 7% faster than
+          // eight, and 1.7% faster than twelve with per-(page, head) scales,
+          // equal per tensor; the general builds spill with more than eight)
+          constexpr int NV = 2 * MD, VDEP = KIND == KIND_F8 && LEAN ? 10 : 8;
           auto vread = [&](int i) -> bf16x8 {
             return v_operand_tr(vstage<true>(buf), trx[i % MD], (uint32_t)((i / MD) * 8192));
           };
