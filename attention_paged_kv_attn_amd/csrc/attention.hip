@@ -1661,17 +1661,21 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
     SmallRegs<KIND, D> r;
     // lane offsets from an opaque copy of the thread id (rebuilt per tile, not spilled)
     auto lane_n = [&]() { int tid = threadIdx.x; asm volatile("" : "+v"(tid)); return tid; };
-    // The next unit's K goes out once this unit's QK has read K, and its V
-    // once this unit's PV has read V.  The next QK waits for both: the
-    // compiler's wait analysis also follows paths of this control flow that
-    // never run (the loop entered without the first tile's loads, K loaded
-    // and V not) and so waits for nearly every load in flight there.  Only K
-    // is needed, but the exact wait (V left in flight through the QK and the
-    // softmax, one more tile's loads outstanding per wave; built with a loop
-    // that no such path reaches) measured 2-4% slower on MI355X for bf16 and
-    // fp8 decode, and an explicit full wait ahead of the tile's scale loads
-    // 1.5% slower for fp8: the memory system does better with fewer requests
-    // in flight here, and the second wave on each SIMD covers the wait.
+    // fp8: the next unit's K goes out once this unit's QK has read K, and its
+    // V once this unit's PV has read V.  bf16: both go out after the PV (a
+    // bf16 tile is twice the bytes; issuing its K after the QK measured 1-1.5%
+    // slower on MI355X at q_len 1 and 2, the fp8 schedule 1% faster than
+    // issuing K late).  Either way the next QK waits for both: the compiler's
+    // wait analysis also follows paths of this control flow that never run
+    // (the loop entered without the first tile's loads, K loaded and V not)
+    // and so waits for nearly every load in flight there.  Only K is needed,
+    // but the exact wait (V left in flight through the QK and the softmax, one
+    // more tile's loads outstanding per wave; built with a loop that no such
+    // path reaches) measured 2-4% slower for bf16 and fp8 decode, and an
+    // explicit full wait ahead of the tile's scale loads 1.5% slower for fp8:
+    // the memory system does better with fewer requests in flight here, and
+    // the second wave on each SIMD covers the wait.
+    constexpr bool k_early = KIND == KIND_F8;
     if (k0 < hi) {
       prepare(tc, sc_, k0, jj);
       const int tid = lane_n();
@@ -1686,7 +1690,7 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
       f32x4 sc[4];
       const float vsc = small_scores<KIND, D, FAST>(p, sc_, x, tc, r, QFromRegs<KIND, D>{qB}, rm, 0, pos_min,
                                                      left_max, st, lane, sc, mixed, ts);
-      if (more) {
+      if (k_early && more) {
         prepare(tn, sn, nk0, nj);
         const int tid = lane_n();
         small_load_k<KIND, D, FAST, kPairedK<KIND>>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
@@ -1694,6 +1698,10 @@ __device__ PA_SEGMENT_FN void heads_range(uint64_t pk, int vw, const WorkerMap w
       small_pv<KIND, D>(r, sc, vsc, st);
       if (more) {
         const int tid = lane_n();
+        if constexpr (!k_early) {
+          prepare(tn, sn, nk0, nj);
+          small_load_k<KIND, D, FAST, kPairedK<KIND>>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
+        }
         small_load_v<KIND, D, FAST>(p, sn, tn, r, tid & 15, (tid >> 4) & 3);
       }
       tc = tn;
