@@ -274,9 +274,10 @@ __device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_
   return *(const PA_GLOBAL u32x2*)(base + soff + voff);
 }
 // temporal 16-byte load: fp8 K rows read in two halves by consecutive loads,
-// and the bf16 K rows of per-kv-head decode streams (small_range), where it
-// measured faster (MTP 4 decode 2%, the hybrid batch 7%; V stays non-temporal
-// there: temporal V was 8% slower)
+// and the bf16 K rows of per-kv-head small Q-blocks (small_range and
+// small_segment), where it measured faster on MI355X (MTP 4 decode 2%, the
+// hybrid batch 7%, a statically split 128K decode 9.5%; V stays
+// non-temporal there: temporal V was 8% slower)
 __device__ __forceinline__ u32x4 gload16t(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL u32x4*)(base + soff + voff);
 }
@@ -1110,7 +1111,7 @@ __device__ __forceinline__ void small_run(const KParams& p, const SeqCtx& s, con
     Tile<C::ELT, FAST> t;
     SmallRegs<KIND, D> r;
     t.init(p, s, tile);
-    small_load_k<KIND, D, FAST>(p, s, t, r, n, h);
+    small_load_k<KIND, D, FAST, false, true>(p, s, t, r, n, h);   // bf16 K temporal (see gload16t)
     small_load_v<KIND, D, FAST>(p, s, t, r, n, h);
     small_compute<KIND, D, FAST>(p, s, x, t, r, QFromLds<KIND, D>{qlds}, rm, bm_head, pos_min, left_max, st, lane);
   }
