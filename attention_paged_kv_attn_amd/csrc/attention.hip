@@ -264,8 +264,9 @@ __device__ __forceinline__ float held(float v) { return __int_as_float(held(__fl
 // The 16-byte load is non-temporal: its users stream K/V rows that are read
 // once (decode tiles), and not allocating them in the caches moved the bf16
 // decode kernel from 5.05 to 5.35 TB/s (NHD) and 5.31 to 5.95 TB/s (HND) on
-// MI355X.  The 8-byte load (the fp8 decode rows) stays temporal: made
-// non-temporal it slowed fp8 decode by 41%.
+// MI355X.  The temporal 8-byte load serves the fp8 K rows of the per-kv-head
+// paths (with 8-byte V rows also temporal, fp8 decode once ran 41% slower
+// non-temporal; the V rows alone non-temporal are faster, see gload8nt).
 #define PA_GLOBAL __attribute__((address_space(1)))
 __device__ __forceinline__ u32x4 gload16(const char* base, uint32_t voff, uint32_t soff) {
   return __builtin_nontemporal_load((const PA_GLOBAL u32x4*)(base + soff + voff));
@@ -280,6 +281,13 @@ __device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_
 // non-temporal there: temporal V was 8% slower)
 __device__ __forceinline__ u32x4 gload16t(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL u32x4*)(base + soff + voff);
+}
+// non-temporal 8-byte load: fp8 V rows (d = 128) and bf16 V rows (d = 64)
+// of decode, each read once; measured 8% faster than temporal for fp8 decode
+// q_len 1 (NHD and HND) and 3% at q_len 4 on MI355X, with the fp8 K rows
+// temporal beside them
+__device__ __forceinline__ u32x2 gload8nt(const char* base, uint32_t voff, uint32_t soff) {
+  return __builtin_nontemporal_load((const PA_GLOBAL u32x2*)(base + soff + voff));
 }
 __device__ __forceinline__ unsigned gload4(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL unsigned*)(base + soff + voff);
@@ -849,7 +857,7 @@ template <int KIND, int MD>
 __device__ __forceinline__ typename VRawT<KIND, MD>::T bload_v(const char* r, uint32_t voff, uint32_t soff) {
   using T = typename VRawT<KIND, MD>::T;
   if constexpr (sizeof(T) == 16) return gload16(r, voff, soff);
-  else if constexpr (sizeof(T) == 8) return gload8(r, voff, soff);
+  else if constexpr (sizeof(T) == 8) return gload8nt(r, voff, soff);
   else return gload4(r, voff, soff);
 }
 
