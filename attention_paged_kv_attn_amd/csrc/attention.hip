@@ -274,11 +274,12 @@ __device__ __forceinline__ u32x4 gload16(const char* base, uint32_t voff, uint32
 __device__ __forceinline__ u32x2 gload8(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL u32x2*)(base + soff + voff);
 }
-// temporal 16-byte load: fp8 K rows read in two halves by consecutive loads,
-// and the bf16 K rows of per-kv-head small Q-blocks (small_range and
-// small_segment), where it measured faster on MI355X (MTP 4 decode 2%, the
-// hybrid batch 7%, a statically split 128K decode 9.5%; V stays
-// non-temporal there: temporal V was 8% slower)
+// temporal 16-byte load: the bf16 K rows of per-kv-head small Q-blocks
+// (small_range and small_segment), where it measured faster on MI355X (MTP 4
+// decode 2%, the hybrid batch 7%, a statically split 128K decode 9.5%; V
+// stays non-temporal there: temporal V was 8% slower).  The sequence-Q-block
+// path keeps its K rows non-temporal, bf16 and paired fp8 alike (temporal:
+// bf16 1.8% slower on HND; fp8 2% slower at q_len 2 and on HND)
 __device__ __forceinline__ u32x4 gload16t(const char* base, uint32_t voff, uint32_t soff) {
   return *(const PA_GLOBAL u32x4*)(base + soff + voff);
 }
@@ -832,7 +833,7 @@ __device__ __forceinline__ void bload_qk(const char* r, uint32_t voff, uint32_t 
   if constexpr (KIND == KIND_F8 && PAIRED) {
 #pragma unroll
     for (int c = 0; c < C::KSQ / 2; ++c) {
-      const u32x4 v = gload16t(r, voff + 64 * c, soff);
+      const u32x4 v = gload16(r, voff + 64 * c, soff);
       op[2 * c] = __builtin_bit_cast(long, u32x2{v[0], v[1]});
       op[2 * c + 1] = __builtin_bit_cast(long, u32x2{v[2], v[3]});
     }
